@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark: paged FP8-E5M2 grouped-query decode attention.
+
+Default workload: the ragged long batch (B=16, Hkv=4, Hq=32, head_dim 128,
+page size 16, context lengths uniform in [2048, 33600], randomly permuted
+pages in a 256K-token-per-sequence pool). A step is one xqa_decode call
+(split kernel + combine kernel) over the whole batch, replayed from a HIP
+graph; R input variants (different lengths, page tables, q and K/V bytes),
+each with its own captured graph, are cycled so inputs change between
+replays and the rotating footprint exceeds the on-package caches.
+
+Order: generate -> upload -> CPU baseline leg (the float64 oracle timed on
+the host cores; its output is also the correctness gate for variant 0) ->
+graph gate (every variant's replay bitwise equal to its eager call) ->
+independent warm-up of each arm -> timed graph replays (the headline) ->
+A/B/B/A eager vs graph blocks -> per-kernel HIP-event timing of the split
+kernel on the stream it is launched on. Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "us per decode step + achieved KV-read HBM GB/s (% of peak), B16 ragged ~17.8K"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", type=int, default=4, help="workload 1..5 (4 = headline)")
+    ap.add_argument("--variants", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=0, help="oracle repetitions (0 = auto, ~10-20 s)")
+    ap.add_argument("--quick", action="store_true", help="skip A/B/B/A and warm-mode extras")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline_leg(w, gpu_out, reps_arg):
+    """Time the float64 oracle on a full decode step; compare it with gpu_out."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    kp, vp = w.pools()
+    t = time.perf_counter()
+    ref = oracle.decode_attention(w.q, kp, vp, w.block_table, w.context_lens, w.scale)
+    one = time.perf_counter() - t
+    reps = reps_arg or max(1, min(20, int(12.0 / max(one, 1e-3))))
+    t = time.perf_counter()
+    for _ in range(reps):
+        oracle.decode_attention(w.q, kp, vp, w.block_table, w.context_lens, w.scale)
+    cpu_s = (time.perf_counter() - t) / reps
+    cpu = {"value": w.kv_bytes / cpu_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"full decode step of {w.name} (sum ctx={w.total_tokens}, {w.kv_bytes} KV bytes), "
+                     f"{reps} repetitions, {cpu_s * 1e6:.0f} us/step; float64 numpy, BLAS threads={threads}"}
+    log(f"cpu oracle: {cpu_s * 1e3:.1f} ms/step ({cpu['value']:.3f} GB/s) x{reps}")
+    # tolerance: |gpu - ref| <= 2e-3 or <= 1e-2 |ref| per element; relative L2 <= 1e-3
+    err = np.abs(gpu_out.astype(np.float64) - ref)
+    ok_el = (err <= 2e-3) | (err <= 1e-2 * np.abs(ref))
+    rel_l2 = float(np.sqrt((err ** 2).sum() / max((ref ** 2).sum(), 1e-300)))
+    fails = int((~ok_el).sum()) + int((~np.isfinite(gpu_out)).sum())
+    gate = {"ok": fails == 0 and rel_l2 <= 1e-3, "fails": fails, "max_abs": float(err.max()),
+            "rel_l2": rel_l2}
+    return cpu, gate
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode step shards by sequence or KV head with no exchange, see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from decode_attention_paged_e5m2_amd import Xqa
+    from workloads import make_config
+    from workloads.device import to_device
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    works = [make_config(args.config, v) for v in range(args.variants)]
+    devs = [to_device(w, dev) for w in works]
+    w0 = works[0]
+    log(f"generated+uploaded {len(works)} variants in {time.time() - t0:.1f}s; "
+        f"Σctx={[w.total_tokens for w in works]}")
+    kv_bytes = [w.kv_bytes for w in works]
+
+    xqa = Xqa(max_batch=w0.batch, num_q_heads=w0.num_q_heads, num_kv_heads=w0.num_kv_heads,
+              max_pages_per_seq=w0.max_pages_per_seq)
+    info = xqa.info
+    stream = torch.cuda.current_stream(dev)
+
+    def call(d, out, fn=None):
+        (fn or xqa.decode)(q=d.q, k_pages=d.k_pages, v_pages=d.v_pages, block_table=d.block_table,
+                           context_lens=d.context_lens, scale=w0.scale, out=out)
+
+    outs = [torch.empty_like(d.q) for d in devs]
+
+    # ------------------------------------------- CPU oracle leg (and gate)
+    # The float64 oracle is timed on the host cores as a reported baseline;
+    # its output doubles as the correctness gate: no timing is admitted for a
+    # GPU result that does not match it.
+    call(devs[0], outs[0])
+    torch.cuda.synchronize()
+    gpu0 = outs[0].float().cpu().numpy()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu, gate = cpu_baseline_leg(w0, gpu0, args.cpu_reps)
+        log(f"oracle gate: {gate}")
+        if not gate["ok"]:
+            print(json.dumps({"error": "parity gate failed", "stats": gate}))
+            return 1
+
+    eager = []
+    for d, o in zip(devs, outs):
+        call(d, o)
+        eager.append(o.clone())
+    torch.cuda.synchronize()
+
+    graphs = []
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):      # warm the capture path off the timed stream
+        for d, o in zip(devs, outs):
+            call(d, o)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    for d, o in zip(devs, outs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(d, o)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i, (g, o) in enumerate(zip(graphs, outs)):
+        o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(o.view(torch.int16), eager[i].view(torch.int16)):
+            print(json.dumps({"error": f"graph replay differs from eager (variant {i})"}))
+            return 1
+    log("graph == eager bitwise on all variants")
+
+    R = len(graphs)
+
+    def run_graph(n_steps, start=0):
+        for s in range(n_steps):
+            graphs[(start + s) % R].replay()
+
+    def run_eager(n_steps, start=0):
+        for s in range(n_steps):
+            i = (start + s) % R
+            call(devs[i], outs[i])
+
+    # ---------------------------------------------------- headline timing
+    run_eager(args.warmup)                 # each arm warms up on its own
+    torch.cuda.synchronize()
+    run_graph(args.warmup)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    run_graph(args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    steps_bytes = sum(kv_bytes[s % R] for s in range(args.steps))
+    gbs = steps_bytes / elapsed / 1e9
+    us_step = elapsed / args.steps * 1e6
+    log(f"graph replay: {us_step:.2f} us/step, {gbs:.1f} GB/s KV ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+
+    detail = {"us_per_step_graph": us_step, "kv_bytes_per_step_mean": statistics.mean(kv_bytes),
+              "handle": info}
+
+    # ------------------------------------------------------ A/B/B/A blocks
+    if not args.quick:
+        blk = max(50, min(500, args.steps // 4))
+        res = {"eager": [], "graph": []}
+        for rep in range(3):
+            for arm in ("eager", "graph", "graph", "eager"):
+                torch.cuda.synchronize()
+                t = time.perf_counter()
+                (run_eager if arm == "eager" else run_graph)(blk)
+                torch.cuda.synchronize()
+                res[arm].append((time.perf_counter() - t) / blk * 1e6)
+        detail["abba_us_per_step"] = {k: {"median": statistics.median(v), "min": min(v), "max": max(v)}
+                                      for k, v in res.items()}
+        # warm mode: the same variant back to back (may be cache resident)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(blk):
+            graphs[0].replay()
+        torch.cuda.synchronize()
+        detail["warm_same_input_us_per_step"] = (time.perf_counter() - t) / blk * 1e6
+
+    # ------------------------------------- per-kernel timing (split kernel)
+    n_ev = max(20, min(200, args.steps // 10))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for k in range(n_ev):
+        i = k % R
+        d = devs[i]
+        ev[k][0].record(stream)
+        call(d, outs[i], fn=xqa.attend)
+        ev[k][1].record(stream)
+        xqa.combine(context_lens=d.context_lens, out=outs[i])
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    attend_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(n_ev)]
+    combine_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(n_ev)]
+    attend_bytes = [kv_bytes[k % R] for k in range(n_ev)]
+    attend_avg_us = statistics.mean(attend_ms) * 1e3
+    achieved = sum(attend_bytes) / (sum(attend_ms) * 1e-3) / 1e9
+    detail["split_kernel_us_mean"] = attend_avg_us
+    detail["split_kernel_us_median"] = statistics.median(attend_ms) * 1e3
+    detail["combine_kernel_us_mean"] = statistics.mean(combine_ms) * 1e3
+    log(f"split kernel: {attend_avg_us:.2f} us mean -> {achieved:.1f} GB/s; "
+        f"combine {detail['combine_kernel_us_mean']:.2f} us")
+
+    line = {
+        "metric": METRIC,
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": us_step / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w0.name.rsplit("_v", 1)[0],
+            "batch": w0.batch, "num_kv_heads": w0.num_kv_heads, "num_q_heads": w0.num_q_heads,
+            "head_dim": w0.head_dim, "page_size": w0.page_size, "kv_dtype": "fp8_e5m2",
+            "context_lens": "variant-dependent; " + ",".join(str(w.total_tokens) for w in works) + " tokens",
+            "variants": R, "timed_as": "hipGraph replay, variants cycled",
+            "pct_of_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+            "us_per_step": us_step,
+        },
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,176 @@
+"""Thin Python binding over libxqa.so: argument checks and marshalling only.
+
+PyTorch provides device memory and the current HIP stream; every step of the
+computation runs in the library's kernels. Optional arguments are keywords.
+"""
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+HEAD_DIM = 128
+PAGE_SIZE = 16
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream], device: torch.device) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+class Xqa:
+    """A decode-attention handle: fixed head counts, capacity and workspace.
+
+    Example::
+
+        xqa = Xqa(max_batch=16, num_q_heads=32, num_kv_heads=4, max_pages_per_seq=16384)
+        out = xqa.decode(q=q, k_pages=k, v_pages=v, block_table=bt,
+                         context_lens=lens, scale=1 / 128 ** 0.5)
+    """
+
+    def __init__(self, *, max_batch: int, num_q_heads: int, num_kv_heads: int,
+                 max_pages_per_seq: int, head_dim: int = HEAD_DIM, page_size: int = PAGE_SIZE,
+                 max_work_items: int = 0, device: Optional[torch.device] = None):
+        lib = _lib.load()
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        cfg = _lib.XqaConfig(max_batch, num_q_heads, num_kv_heads, head_dim, page_size,
+                             max_pages_per_seq, max_work_items)
+        handle = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _lib.check(lib.xqa_create(ctypes.byref(cfg), ctypes.byref(handle)))
+        self._h = handle
+        self.max_batch = max_batch
+        self.num_q_heads = num_q_heads
+        self.num_kv_heads = num_kv_heads
+        self.max_pages_per_seq = max_pages_per_seq
+        self.head_dim = head_dim
+        self.page_size = page_size
+
+    # ----------------------------------------------------------------- info
+    @property
+    def info(self) -> dict:
+        inf = _lib.XqaInfo()
+        _lib.check(_lib.load().xqa_get_info(self._h, ctypes.byref(inf)))
+        return {k: getattr(inf, k) for k, _ in _lib.XqaInfo._fields_}
+
+    def plan(self, context_lens) -> Tuple[int, int]:
+        """Host mirror of the device plan: (split length in tokens, work items)."""
+        lens = [int(x) for x in (context_lens.tolist() if hasattr(context_lens, "tolist")
+                                 else context_lens)]
+        arr = (ctypes.c_int32 * len(lens))(*lens)
+        S, items = ctypes.c_int32(), ctypes.c_int32()
+        _lib.check(_lib.load().xqa_plan(self._h, arr, len(lens), ctypes.byref(S), ctypes.byref(items)))
+        return S.value, items.value
+
+    # ------------------------------------------------------------ checking
+    def _check(self, q, k_pages, v_pages, block_table, context_lens, out, batch):
+        dev = self.device
+        for name, t, dt in (("q", q, torch.float16), ("k_pages", k_pages, torch.uint8),
+                            ("v_pages", v_pages, torch.uint8), ("block_table", block_table, torch.int32),
+                            ("context_lens", context_lens, torch.int32), ("out", out, torch.float16)):
+            _need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+            _need(t.dtype == dt, f"{name} must be {dt}, got {t.dtype}")
+            _need(t.device == dev, f"{name} must be on {dev}, got {t.device}")
+            _need(t.is_contiguous(), f"{name} must be contiguous")
+        Hq, Hkv, D, P = self.num_q_heads, self.num_kv_heads, self.head_dim, self.page_size
+        _need(q.dim() == 3 and q.shape[1:] == (Hq, D) and q.shape[0] >= batch,
+              f"q must be [>= batch, {Hq}, {D}], got {tuple(q.shape)}")
+        _need(out.dim() == 3 and out.shape[1:] == (Hq, D) and out.shape[0] >= batch,
+              f"out must be [>= batch, {Hq}, {D}], got {tuple(out.shape)}")
+        _need(k_pages.dim() == 4 and k_pages.shape[1:] == (Hkv, P, D),
+              f"k_pages must be [num_pages, {Hkv}, {P}, {D}], got {tuple(k_pages.shape)}")
+        _need(v_pages.shape == k_pages.shape, "v_pages must have k_pages' shape")
+        _need(block_table.dim() == 2 and block_table.shape[1] == self.max_pages_per_seq
+              and block_table.shape[0] >= batch,
+              f"block_table must be [>= batch, {self.max_pages_per_seq}], got {tuple(block_table.shape)}")
+        _need(context_lens.dim() == 1 and context_lens.shape[0] >= batch,
+              "context_lens must be [>= batch]")
+        _need(1 <= batch <= self.max_batch, f"batch must be in [1, {self.max_batch}]")
+
+    def _args(self, q, k_pages, v_pages, block_table, context_lens, out, batch, scale, stream):
+        if batch is None:
+            batch = q.shape[0]
+        if out is None:
+            out = torch.empty_like(q)
+        self._check(q, k_pages, v_pages, block_table, context_lens, out, batch)
+        scale = float(scale)
+        _need(math.isfinite(scale), "scale must be finite")
+        return out, (self._h, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                     _ptr(context_lens), int(batch), ctypes.c_float(scale), _ptr(out),
+                     _stream_ptr(stream, self.device))
+
+    # -------------------------------------------------------------- decode
+    def decode(self, *, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+               block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+               out: Optional[torch.Tensor] = None, batch: Optional[int] = None,
+               stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """One decode step (split + combine kernels) on the current stream."""
+        out, args = self._args(q, k_pages, v_pages, block_table, context_lens, out, batch, scale, stream)
+        _lib.check(_lib.load().xqa_decode(*args))
+        return out
+
+    def attend(self, *, q, k_pages, v_pages, block_table, context_lens, scale, out=None,
+               batch=None, stream=None) -> torch.Tensor:
+        """First stage only (see xqa_decode_attend); combine() must follow."""
+        out, args = self._args(q, k_pages, v_pages, block_table, context_lens, out, batch, scale, stream)
+        _lib.check(_lib.load().xqa_decode_attend(*args))
+        return out
+
+    def combine(self, *, context_lens, out, batch=None, stream=None) -> torch.Tensor:
+        """Second stage only (see xqa_decode_combine)."""
+        if batch is None:
+            batch = out.shape[0]
+        _need(context_lens.dtype == torch.int32 and context_lens.device == self.device,
+              "context_lens must be int32 on the handle's device")
+        _need(out.dtype == torch.float16 and out.device == self.device and out.is_contiguous(),
+              "out must be contiguous float16 on the handle's device")
+        _need(out.dim() == 3 and out.shape[1:] == (self.num_q_heads, self.head_dim)
+              and out.shape[0] >= batch and context_lens.shape[0] >= batch, "bad shapes")
+        _lib.check(_lib.load().xqa_decode_combine(self._h, _ptr(context_lens), int(batch), _ptr(out),
+                                                  _stream_ptr(stream, self.device)))
+        return out
+
+    # ----------------------------------------------------------- lifetime
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value is not None:
+            _lib.check(_lib.load().xqa_destroy(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def debug_widen_e5m2(codes: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
+    """Widen uint8 E5M2 codes on the GPU with the kernels' own routine.
+
+    Returns (binary16 bit patterns as int16, values as float32).
+    """
+    _need(codes.dtype == torch.uint8 and codes.is_cuda and codes.is_contiguous(),
+          "codes must be a contiguous uint8 GPU tensor")
+    bits = torch.empty(codes.shape, dtype=torch.int16, device=codes.device)
+    vals = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    _lib.check(_lib.load().xqa_debug_widen_e5m2(_ptr(codes), _ptr(bits), _ptr(vals), codes.numel(),
+                                                _stream_ptr(stream, codes.device)))
+    return bits, vals

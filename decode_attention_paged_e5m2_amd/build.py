@@ -1,0 +1,69 @@
+"""Build libxqa.so (the HIP kernels + C-ABI) in-tree for gfx950 with hipcc."""
+
+import os
+import subprocess
+import sys
+import tempfile
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+REPO_DIR = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(REPO_DIR, "include")
+LIB_NAME = "libxqa.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+SOURCES = [os.path.join(CSRC, "xqa_kernels.hip"), os.path.join(CSRC, "xqa_api.cpp")]
+ARCH = "gfx950"
+
+# Packed-FP32 instructions are disabled for all device code.
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE,
+]
+
+
+def hipcc() -> str:
+    for cand in ("/opt/rocm/bin/hipcc", "hipcc"):
+        if os.path.isabs(cand) and os.path.exists(cand):
+            return cand
+    return "hipcc"
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the shared library; returns its path. Raises on failure."""
+    fd, tmp = tempfile.mkstemp(prefix=".libxqa.", suffix=".so.tmp", dir=PKG_DIR)
+    os.close(fd)
+    cmd = [hipcc()] + COMMON_FLAGS + ["-shared", "-o", tmp] + SOURCES
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+        if verbose and res.stderr.strip():
+            # hipcc's host pass does not know the packed-fp32 feature; that note is harmless.
+            lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
+            if lines:
+                print("\n".join(lines), file=sys.stderr)
+        os.replace(tmp, LIB_PATH)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return LIB_PATH
+
+
+def resource_usage() -> str:
+    """Compiler report of VGPR/AGPR/SGPR/LDS/scratch per kernel (our own build)."""
+    cmd = [hipcc()] + COMMON_FLAGS + ["--offload-device-only", "-c", "-o", os.devnull,
+                                      "-Rpass-analysis=kernel-resource-usage", SOURCES[0]]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(res.stderr)
+    keep = [l for l in res.stderr.splitlines() if "remark" in l]
+    return "\n".join(keep)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    if "--resources" in sys.argv:
+        print(resource_usage())

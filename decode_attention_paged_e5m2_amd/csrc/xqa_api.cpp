@@ -1,0 +1,294 @@
+// C-ABI entry points: argument validation, handle and workspace, launches.
+// Every check runs before any HIP call, so a rejected call launches nothing
+// (fail-closed, as the page "[Kernel][SM70] Fold DeepSeek V4 MXFP4 decode
+// exponents" asks of admission code in its audit comments: explicit errors,
+// never a silent no-launch, no environment reads in native code).
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/xqa.h"
+#include "xqa_internal.h"
+
+struct xqa_handle_s {
+  xqa_config_t cfg;
+  int device;
+  int grid;          // split workgroups = work-item capacity
+  int per_head;      // grid / Hkv
+  int item_stride;   // floats per partial record
+  float* partials;
+  size_t workspace_bytes;
+};
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+xqa_status_t fail(xqa_status_t st, const char* fmt, const char* detail = nullptr) {
+  if (detail) {
+    snprintf(g_last_error, sizeof(g_last_error), fmt, detail);
+  } else {
+    snprintf(g_last_error, sizeof(g_last_error), "%s", fmt);
+  }
+  return st;
+}
+
+xqa_status_t hip_fail(hipError_t e, const char* where) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
+  return XQA_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+xqa_status_t check_decode_args(xqa_handle_t h, const void* q, const uint8_t* k_pages,
+                               const uint8_t* v_pages, const int32_t* block_table,
+                               const int32_t* context_lens, int32_t batch, float scale,
+                               const void* out) {
+  if (!h) return fail(XQA_ERR_INVALID_ARG, "null handle");
+  if (!q || !k_pages || !v_pages || !block_table || !context_lens || !out)
+    return fail(XQA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16))
+    return fail(XQA_ERR_INVALID_ARG, "q, k_pages, v_pages and out must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4))
+    return fail(XQA_ERR_INVALID_ARG, "block_table and context_lens must be 4-byte aligned");
+  if (batch < 1 || batch > h->cfg.max_batch)
+    return fail(XQA_ERR_INVALID_ARG, "batch outside [1, max_batch]");
+  if (!isfinite(scale)) return fail(XQA_ERR_INVALID_ARG, "scale must be finite");
+  return XQA_OK;
+}
+
+xqa_status_t check_device(xqa_handle_t h) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != h->device)
+    return fail(XQA_ERR_INVALID_ARG, "current device differs from the handle's device");
+  return XQA_OK;
+}
+
+xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_pages,
+                            const uint8_t* v_pages, const int32_t* block_table,
+                            const int32_t* context_lens, int32_t batch, float scale, void* out) {
+  xqa::AttendArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.partials = h->partials;
+  a.batch = batch;
+  a.num_kv_heads = h->cfg.num_kv_heads;
+  a.group = h->cfg.num_q_heads / h->cfg.num_kv_heads;
+  a.max_pages = h->cfg.max_pages_per_seq;
+  a.max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
+  a.per_head = h->per_head;
+  a.item_stride = h->item_stride;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  return a;
+}
+
+xqa::CombineArgs combine_args(xqa_handle_t h, const int32_t* context_lens, int32_t batch,
+                              void* out) {
+  xqa::CombineArgs c;
+  c.context_lens = context_lens;
+  c.partials = h->partials;
+  c.out = static_cast<uint16_t*>(out);
+  c.batch = batch;
+  c.num_kv_heads = h->cfg.num_kv_heads;
+  c.group = h->cfg.num_q_heads / h->cfg.num_kv_heads;
+  c.max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
+  c.per_head = h->per_head;
+  c.item_stride = h->item_stride;
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* xqa_status_string(xqa_status_t s) {
+  switch (s) {
+    case XQA_OK: return "XQA_OK";
+    case XQA_ERR_INVALID_ARG: return "XQA_ERR_INVALID_ARG";
+    case XQA_ERR_UNSUPPORTED: return "XQA_ERR_UNSUPPORTED";
+    case XQA_ERR_OUT_OF_MEMORY: return "XQA_ERR_OUT_OF_MEMORY";
+    case XQA_ERR_HIP: return "XQA_ERR_HIP";
+  }
+  return "XQA_ERR_UNKNOWN";
+}
+
+const char* xqa_last_error(void) { return g_last_error; }
+
+xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
+  if (!cfg || !out_handle) return fail(XQA_ERR_INVALID_ARG, "null cfg or out_handle");
+  if (cfg->max_batch < 1 || cfg->num_q_heads < 1 || cfg->num_kv_heads < 1 ||
+      cfg->max_pages_per_seq < 1 || cfg->max_work_items < 0)
+    return fail(XQA_ERR_INVALID_ARG, "sizes must be positive");
+  if (cfg->head_dim != xqa::kHeadDim) return fail(XQA_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (cfg->page_size != xqa::kPageSize) return fail(XQA_ERR_UNSUPPORTED, "page_size must be 16");
+  if (cfg->num_q_heads % cfg->num_kv_heads != 0)
+    return fail(XQA_ERR_UNSUPPORTED, "num_q_heads must be a multiple of num_kv_heads");
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  if (G > xqa::kMaxGroup) return fail(XQA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+  if ((long long)cfg->max_pages_per_seq * xqa::kPageSize > (1LL << 30))
+    return fail(XQA_ERR_UNSUPPORTED, "max_pages_per_seq too large");
+  if (cfg->max_batch >= xqa::kMaxItemsPerHead)
+    return fail(XQA_ERR_UNSUPPORTED, "max_batch must be below 2048");
+  const long long min_grid = (long long)cfg->num_kv_heads * (cfg->max_batch + 1);
+  const long long max_grid = (long long)cfg->num_kv_heads * xqa::kMaxItemsPerHead;
+  if (cfg->max_work_items > 0 &&
+      (cfg->max_work_items < min_grid || cfg->max_work_items > max_grid))
+    return fail(XQA_ERR_INVALID_ARG,
+                "max_work_items must lie in [Hkv*(max_batch+1), Hkv*2048]");
+
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  int per_cu = 0;
+  e = xqa::attend_blocks_per_cu(&per_cu);
+  if (e != hipSuccess) return hip_fail(e, "occupancy query");
+  if (per_cu < 1) per_cu = 1;
+
+  long long grid = cfg->max_work_items;
+  if (grid == 0) {
+    // Every item resident at once: one round of equal-sized items.
+    grid = (long long)cus * per_cu;
+    if (grid < min_grid) grid = min_grid;
+    if (grid > max_grid) grid = max_grid;
+  }
+  const int per_head = (int)(grid / cfg->num_kv_heads);
+  grid = (long long)per_head * cfg->num_kv_heads;
+  const int stride = ((G * (xqa::kHeadDim + 2)) + 3) / 4 * 4;
+  const size_t ws = (size_t)grid * stride * sizeof(float);
+
+  xqa_handle_s* h = new (std::nothrow) xqa_handle_s();
+  if (!h) return fail(XQA_ERR_OUT_OF_MEMORY, "host allocation failed");
+  h->cfg = *cfg;
+  h->device = dev;
+  h->grid = (int)grid;
+  h->per_head = per_head;
+  h->item_stride = stride;
+  h->workspace_bytes = ws;
+  h->partials = nullptr;
+  e = hipMalloc(reinterpret_cast<void**>(&h->partials), ws);
+  if (e != hipSuccess) {
+    delete h;
+    if (e == hipErrorOutOfMemory) return fail(XQA_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+    return hip_fail(e, "hipMalloc");
+  }
+  *out_handle = h;
+  return XQA_OK;
+}
+
+xqa_status_t xqa_destroy(xqa_handle_t h) {
+  if (!h) return XQA_OK;
+  hipError_t e = hipSuccess;
+  if (h->partials) e = hipFree(h->partials);
+  delete h;
+  if (e != hipSuccess) return hip_fail(e, "hipFree");
+  return XQA_OK;
+}
+
+xqa_status_t xqa_get_info(xqa_handle_t h, xqa_info_t* info) {
+  if (!h || !info) return fail(XQA_ERR_INVALID_ARG, "null handle or info");
+  info->device = h->device;
+  info->max_work_items = h->grid;
+  info->items_per_head = h->per_head;
+  info->token_granule = xqa::kGranule;
+  info->threads_per_item = xqa::kThreads;
+  info->item_stride_floats = h->item_stride;
+  info->workspace_bytes = (int64_t)h->workspace_bytes;
+  return XQA_OK;
+}
+
+xqa_status_t xqa_decode_attend(xqa_handle_t h, const void* q, const uint8_t* k_pages,
+                               const uint8_t* v_pages, const int32_t* block_table,
+                               const int32_t* context_lens, int32_t batch, float scale,
+                               void* out, void* stream) {
+  xqa_status_t st =
+      check_decode_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
+  if (st != XQA_OK) return st;
+  if ((st = check_device(h)) != XQA_OK) return st;
+  const xqa::AttendArgs a =
+      attend_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
+  hipError_t e = xqa::launch_attend(a, h->grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+  return XQA_OK;
+}
+
+xqa_status_t xqa_decode_combine(xqa_handle_t h, const int32_t* context_lens, int32_t batch,
+                                void* out, void* stream) {
+  if (!h) return fail(XQA_ERR_INVALID_ARG, "null handle");
+  if (!context_lens || !out) return fail(XQA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned(out, 16) || !aligned(context_lens, 4))
+    return fail(XQA_ERR_INVALID_ARG, "misaligned pointer");
+  if (batch < 1 || batch > h->cfg.max_batch)
+    return fail(XQA_ERR_INVALID_ARG, "batch outside [1, max_batch]");
+  xqa_status_t st = check_device(h);
+  if (st != XQA_OK) return st;
+  const xqa::CombineArgs c = combine_args(h, context_lens, batch, out);
+  hipError_t e = xqa::launch_combine(c, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return XQA_OK;
+}
+
+xqa_status_t xqa_decode(xqa_handle_t h, const void* q, const uint8_t* k_pages,
+                        const uint8_t* v_pages, const int32_t* block_table,
+                        const int32_t* context_lens, int32_t batch, float scale, void* out,
+                        void* stream) {
+  xqa_status_t st =
+      check_decode_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
+  if (st != XQA_OK) return st;
+  if ((st = check_device(h)) != XQA_OK) return st;
+  const xqa::AttendArgs a =
+      attend_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = xqa::launch_attend(a, h->grid, s);
+  if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+  e = xqa::launch_combine(combine_args(h, context_lens, batch, out), s);
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return XQA_OK;
+}
+
+xqa_status_t xqa_plan(xqa_handle_t h, const int32_t* ctx, int32_t batch, int32_t* split_tokens,
+                      int32_t* num_items) {
+  if (!h || !ctx || !split_tokens || !num_items)
+    return fail(XQA_ERR_INVALID_ARG, "null argument");
+  if (batch < 1 || batch > h->cfg.max_batch)
+    return fail(XQA_ERR_INVALID_ARG, "batch outside [1, max_batch]");
+  const int max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
+  long long n_tot = 0;
+  int active = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int n = xqa::clamp_len(ctx[b], max_tokens);
+    n_tot += n;
+    active += n > 0;
+  }
+  const int S = xqa::split_tokens(n_tot, active, h->per_head);
+  long long items = 0;
+  for (int b = 0; b < batch; ++b) items += xqa::num_splits(xqa::clamp_len(ctx[b], max_tokens), S);
+  *split_tokens = S;
+  *num_items = (int32_t)(items * h->cfg.num_kv_heads);
+  return XQA_OK;
+}
+
+xqa_status_t xqa_debug_widen_e5m2(const uint8_t* in, uint16_t* out_f16, float* out_f32, int64_t n,
+                                  void* stream) {
+  if (!in || (!out_f16 && !out_f32)) return fail(XQA_ERR_INVALID_ARG, "null pointer");
+  if (n < 0) return fail(XQA_ERR_INVALID_ARG, "negative count");
+  if ((out_f16 && !aligned(out_f16, 2)) || (out_f32 && !aligned(out_f32, 4)))
+    return fail(XQA_ERR_INVALID_ARG, "misaligned output");
+  if (n == 0) return XQA_OK;
+  hipError_t e = xqa::launch_widen(in, out_f16, out_f32, n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "widen kernel launch");
+  return XQA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,540 @@
+// Paged FP8-E5M2 grouped-query decode attention: gfx950 kernels.
+//
+// What is computed follows the page "[Kernel][SM70] Pipeline batched E5M2
+// XQA decode" (Purpose; Pending work and gates): one query token per
+// sequence attends over its paged E5M2 K/V cache, query heads sharing KV
+// heads. The phases that page lists -- K load + E5M2 conversion, QK, V load
+// + conversion, PV, synchronisation -- map onto the code below; the tiling
+// is designed for CDNA4 (64-wide waves, MFMA, DPP) rather than taken from it.
+//
+// Split kernel (one workgroup = one work item = (sequence, KV head, token
+// range); four waves take interleaved 32-token blocks = 2 pages):
+//
+//   K: lane l reads token l%16 of the page, head-dim bytes
+//      [16q, 16q+16) and [64+16q, 64+16q+16) (q = l/16): two 16-byte loads
+//      per page, each instruction covering 64 contiguous bytes of all 16
+//      token rows. Widening is one v_perm_b32 per two codes (the E5M2 code is
+//      the high byte of its binary16 value).
+//   QK: S^T = K . Q^T with v_mfma_f32_16x16x32_f16, M = the 16 tokens of a
+//      page, N = the query heads of the group (padded to 16), four MFMAs
+//      over head_dim 128. The contraction index may be permuted freely as
+//      long as the K and Q fragments agree, which is what lets K go straight
+//      from its load layout into the A operand.
+//   Softmax: the accumulator gives lane l the scores of head l%16 for
+//      tokens 4q..4q+3; the block max over a 32-token block is a register
+//      max plus two lane-xor steps (16, 32). Scores are kept in base-2 units
+//      (scale * log2 e folded in) and exponentiated with v_exp_f32.
+//   PV: O^T = V^T . P^T with v_mfma_f32_16x16x32_f16 over the 32 tokens of
+//      the block. P^T needs no data movement: the QK accumulator is already
+//      the B-operand layout once converted to binary16. V^T does: V's
+//      contraction axis (tokens) is strided in memory, so each quad of lanes
+//      loads four token rows and transposes the 4x4 byte tile with two DPP
+//      quad permutes and three v_perm_b32, the last two of which also widen
+//      the bytes to binary16.
+//   The four waves' (max, sum, O) states merge in LDS; a sequence that fits
+//   one item is normalised and written directly, otherwise the item's state
+//   goes to the workspace and the combine kernel merges the splits.
+//
+// Combine kernel: per (sequence, query head, 32-column chunk), the exact
+// log-sum-exp merge M = max m_s, L = sum l_s 2^(m_s-M),
+// out = sum 2^(m_s-M) O_s / L in a fixed order, so results are bitwise
+// reproducible run to run, between eager calls and graph replays, and under
+// any permutation of the physical pages.
+
+#include <math.h>
+
+#include "xqa_internal.h"
+
+namespace xqa {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ widening
+// v_perm_b32 selector bytes 0..3 pick bytes of the second source, 4..7 bytes
+// of the first, 0x0C yields 0x00. Each result holds two binary16 values whose
+// high bytes are the E5M2 codes and whose low bytes are zero.
+__device__ __forceinline__ uint32_t widen_lo(uint32_t x) {   // codes 0, 1 of x
+  return __builtin_amdgcn_perm(0u, x, 0x010C000Cu);
+}
+__device__ __forceinline__ uint32_t widen_hi(uint32_t x) {   // codes 2, 3 of x
+  return __builtin_amdgcn_perm(0u, x, 0x030C020Cu);
+}
+
+// 4x4 byte transpose across a lane quad plus widening. Lane i of the quad
+// holds x = row i (4 consecutive head-dim codes of token i); on return it
+// holds column i as binary16 pairs: h0 = (row0, row1), h1 = (row2, row3).
+// Stage 1 swaps 16-bit halves with lane i^2, stage 2 bytes with lane i^1.
+__device__ __forceinline__ void transpose_widen(uint32_t x, uint32_t sel1, uint32_t selh0,
+                                                uint32_t selh1, uint32_t& h0, uint32_t& h1) {
+  const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  const uint32_t t = __builtin_amdgcn_perm(y, x, sel1);
+  const uint32_t z = (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  h0 = __builtin_amdgcn_perm(z, t, selh0);
+  h1 = __builtin_amdgcn_perm(z, t, selh1);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t pack_half2(float a, float b) {
+  half2v h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// ---------------------------------------------------------------- the plan
+struct Totals {
+  long long n_tot;
+  int active;
+};
+
+__device__ Totals plan_totals(const int32_t* ctx, int batch, int max_tokens, int lane) {
+  long long sum = 0;
+  int cnt = 0;
+  for (int base = 0; base < batch; base += 64) {
+    const int i = base + lane;
+    const int n = i < batch ? clamp_len(ctx[i], max_tokens) : 0;
+    sum += n;
+    cnt += n > 0;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    sum += __shfl_xor(sum, off);
+    cnt += __shfl_xor(cnt, off);
+  }
+  return {sum, cnt};
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Work index j (item / Hkv) -> (sequence b, split s, splits of b).
+__device__ bool plan_locate(const int32_t* ctx, int batch, int max_tokens, int S, int j, int lane,
+                            int& b, int& s, int& nsb) {
+  int prefix = 0;
+  for (int base = 0; base < batch; base += 64) {
+    const int i = base + lane;
+    const int ns = i < batch ? num_splits(clamp_len(ctx[i], max_tokens), S) : 0;
+    const int incl = wave_inclusive_scan(ns, lane);
+    const int lo = prefix + incl - ns;
+    const unsigned long long hit = __ballot(j >= lo && j < prefix + incl);
+    if (hit) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      b = base + src;
+      nsb = __shfl(ns, src);
+      s = j - __shfl(lo, src);
+      return true;
+    }
+    prefix += __shfl(incl, 63);
+  }
+  return false;
+}
+
+// Sequence b -> (splits of b, work index of its first split).
+__device__ void plan_row(const int32_t* ctx, int batch, int max_tokens, int S, int b, int lane,
+                         int& nsb, int& first) {
+  int prefix = 0;
+  nsb = 0;
+  first = 0;
+  for (int base = 0; base < batch; base += 64) {
+    const int i = base + lane;
+    const int ns = i < batch ? num_splits(clamp_len(ctx[i], max_tokens), S) : 0;
+    const int incl = wave_inclusive_scan(ns, lane);
+    if (b < base + 64) {
+      const int src = b - base;
+      nsb = __shfl(ns, src);
+      first = prefix + __shfl(incl - ns, src);
+      return;
+    }
+    prefix += __shfl(incl, 63);
+  }
+}
+
+// ------------------------------------------------------------ split kernel
+struct RawBlock {
+  u32x4 k[4];   // page a: loads 0, 1; page b: loads 2, 3
+  u32x4 v[4];
+};
+
+struct WaveState {
+  float4v o[8];   // O^T tiles: lane (head l%16, q = l/16) holds d = 64L + 16q + 4k + 0..3
+  float4v l;      // running sum of weights of head l%16 (all four entries equal)
+  float m;        // running max of the base-2 scores of head l%16
+};
+
+__device__ __forceinline__ void load_block(RawBlock& r, const uint8_t* ka, const uint8_t* kb,
+                                           const uint8_t* va, const uint8_t* vb, int koff,
+                                           int voff) {
+  r.k[0] = *(const u32x4*)(ka + koff);
+  r.k[1] = *(const u32x4*)(ka + koff + 64);
+  r.k[2] = *(const u32x4*)(kb + koff);
+  r.k[3] = *(const u32x4*)(kb + koff + 64);
+  r.v[0] = *(const u32x4*)(va + voff);
+  r.v[1] = *(const u32x4*)(va + voff + 64);
+  r.v[2] = *(const u32x4*)(vb + voff);
+  r.v[3] = *(const u32x4*)(vb + voff + 64);
+}
+
+template <bool kTail>
+__device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4], WaveState& st,
+                                              float scale_log2e, int tok0, int t_end, int lane,
+                                              uint32_t sel1, uint32_t selh0, uint32_t selh1) {
+  const int q = lane >> 4;
+  if (kTail) {
+    // V rows of tokens past the end are zeroed (their bytes may be NaN codes
+    // and 0 * NaN would poison the sum). V lane token: 4q + (lane & 3).
+    const int tv = tok0 + 4 * q + (lane & 3);
+    if (tv >= t_end) {
+      r.v[0] = u32x4{0, 0, 0, 0};
+      r.v[1] = u32x4{0, 0, 0, 0};
+    }
+    if (tv + kPageSize >= t_end) {
+      r.v[2] = u32x4{0, 0, 0, 0};
+      r.v[3] = u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // QK^T for the group, page a and page b.
+  float4v sa = {0.f, 0.f, 0.f, 0.f};
+  float4v sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 ka = r.k[i >> 1];
+    const u32x4 kb = r.k[2 + (i >> 1)];
+    const uint32_t a0 = ka[(i & 1) * 2], a1 = ka[(i & 1) * 2 + 1];
+    const uint32_t b0 = kb[(i & 1) * 2], b1 = kb[(i & 1) * 2 + 1];
+    const u32x4 fa = {widen_lo(a0), widen_hi(a0), widen_lo(a1), widen_hi(a1)};
+    const u32x4 fb = {widen_lo(b0), widen_hi(b0), widen_lo(b1), widen_hi(b1)};
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, fa), qf[i], sa, 0, 0, 0);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, fb), qf[i], sb, 0, 0, 0);
+  }
+
+  // Scale (base 2), mask, online softmax.
+  float z[8];
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    z[r4] = sa[r4] * scale_log2e;
+    z[4 + r4] = sb[r4] * scale_log2e;
+  }
+  if (kTail) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int t = tok0 + 4 * q + r4;
+      if (t >= t_end) z[r4] = -INFINITY;
+      if (t + kPageSize >= t_end) z[4 + r4] = -INFINITY;
+    }
+  }
+  float bm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                   fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float m_new = fmaxf(st.m, bm);
+  const float alpha = exp2_fast(st.m - m_new);
+  st.m = m_new;
+
+  u32x4 pf;
+#pragma unroll
+  for (int r2 = 0; r2 < 4; ++r2) {
+    pf[r2] = pack_half2(exp2_fast(z[2 * r2] - m_new), exp2_fast(z[2 * r2 + 1] - m_new));
+  }
+  if (__any(alpha != 1.0f)) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.o[t] *= alpha;
+    st.l *= alpha;
+  }
+
+  // PV: V^T tiles from the quad transpose, P^T straight from the scores.
+  const half8 pfrag = __builtin_bit_cast(half8, pf);
+  // Row sums of the same binary16 weights, on the matrix core: an all-ones A
+  // operand makes every output row the sum over the block's 32 tokens, so
+  // each lane receives its head's total without a cross-lane reduction and
+  // the sum is accumulated and rescaled exactly like O.
+  const half8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                      (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+  st.l = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pfrag, st.l, 0, 0, 0);
+#pragma unroll
+  for (int L = 0; L < 2; ++L) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t a0, a1, b0, b1;
+      transpose_widen(r.v[L][k], sel1, selh0, selh1, a0, a1);
+      transpose_widen(r.v[2 + L][k], sel1, selh0, selh1, b0, b1);
+      const u32x4 vf = {a0, a1, b0, b1};
+      st.o[L * 4 + k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, vf), pfrag,
+                                                             st.o[L * 4 + k], 0, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
+  __shared__ float s_m[kWaves][kMaxGroup];
+  __shared__ float s_l[kWaves][kMaxGroup];
+  __shared__ float s_o[kWaves][kMaxGroup][kHeadDim + 4];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+
+  const Totals tt = plan_totals(a.context_lens, a.batch, a.max_tokens, lane);
+  const int S = split_tokens(tt.n_tot, tt.active, a.per_head);
+  const int item = blockIdx.x;
+  const int h = item % a.num_kv_heads;
+  int b, s, nsb;
+  if (!plan_locate(a.context_lens, a.batch, a.max_tokens, S, item / a.num_kv_heads, lane, b, s,
+                   nsb)) {
+    return;   // beyond the planned items: the whole workgroup leaves
+  }
+  const int n = clamp_len(a.context_lens[b], a.max_tokens);
+  const int t_begin = s * S;
+  const int t_end = min(n, t_begin + S);
+  const int G = a.group;
+  const int g = lane & 15;
+  const int q = lane >> 4;
+
+  // Q^T fragments: lane (head g, quarter q) holds, for MFMA i, the eight
+  // head-dim values 64*(i/2) + 16q + 8*(i%2) + 0..7, matching the K bytes.
+  half8 qf[4];
+  if (g < G) {
+    const uint16_t* qrow = a.q + ((long long)b * a.num_kv_heads * G + (long long)h * G + g) * kHeadDim;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qf[i] = *(const half8*)(qrow + 64 * (i >> 1) + 16 * q + 8 * (i & 1));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qf[i] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  const int koff = g * kHeadDim + 16 * q;
+  const int voff = (4 * q + (lane & 3)) * kHeadDim + 16 * ((lane >> 2) & 3);
+  const uint32_t sel1 = (lane & 2) ? 0x03020706u : 0x05040100u;
+  const uint32_t selh0 = (lane & 1) ? 0x010C050Cu : 0x040C000Cu;
+  const uint32_t selh1 = (lane & 1) ? 0x030C070Cu : 0x060C020Cu;
+
+  WaveState st;
+  st.m = -INFINITY;
+  st.l = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) st.o[t] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* bt = a.block_table + (long long)b * a.max_pages;
+  const size_t page_stride = (size_t)a.num_kv_heads * kPageHeadBytes;
+  const size_t head_off = (size_t)h * kPageHeadBytes;
+  const int nblocks = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
+  const int my_blocks = nblocks > wave ? (nblocks - wave + kWaves - 1) / kWaves : 0;
+
+  if (my_blocks > 0) {
+    auto load = [&](RawBlock& r, int j) {
+      const int tok0 = t_begin + j * kBlockTokens;
+      const int pa = bt[tok0 >> 4];
+      const int pb = (tok0 + kPageSize < t_end) ? bt[(tok0 >> 4) + 1] : pa;
+      const size_t oa = (size_t)pa * page_stride + head_off;
+      const size_t ob = (size_t)pb * page_stride + head_off;
+      load_block(r, a.k_pages + oa, a.k_pages + ob, a.v_pages + oa, a.v_pages + ob, koff, voff);
+    };
+    RawBlock cur, nxt;
+    int j = wave;
+    load(cur, j);
+    for (int it = 0; it + 1 < my_blocks; ++it) {
+      load(nxt, j + kWaves);
+      process_block<false>(cur, qf, st, a.scale_log2e, t_begin + j * kBlockTokens, t_end, lane,
+                           sel1, selh0, selh1);
+      cur = nxt;
+      j += kWaves;
+    }
+    process_block<true>(cur, qf, st, a.scale_log2e, t_begin + j * kBlockTokens, t_end, lane, sel1,
+                        selh0, selh1);
+  }
+
+  // Publish the wave's state.
+  if (g < G) {
+    if (q == 0) {
+      s_m[wave][g] = st.m;
+      s_l[wave][g] = st.l[0];
+    }
+#pragma unroll
+    for (int L = 0; L < 2; ++L) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        *(float4v*)&s_o[wave][g][64 * L + 16 * q + 4 * k] = st.o[L * 4 + k];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Merge the four waves (fixed order) and emit the item's result.
+  for (int e = threadIdx.x; e < G * 32; e += kThreads) {
+    const int gg = e >> 5;
+    const int d4 = (e & 31) * 4;
+    float M = s_m[0][gg];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][gg]);
+    float Ls = 0.f;
+    float4v o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = s_m[w][gg];
+      const float f = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
+      Ls += f * s_l[w][gg];
+      o += f * *(const float4v*)&s_o[w][gg][d4];
+    }
+    if (nsb == 1) {
+      const float inv = 1.0f / Ls;
+      uint2 packed;
+      packed.x = pack_half2(o[0] * inv, o[1] * inv);
+      packed.y = pack_half2(o[2] * inv, o[3] * inv);
+      uint16_t* orow = a.out + ((long long)b * a.num_kv_heads * G + (long long)h * G + gg) * kHeadDim;
+      *(uint2*)(orow + d4) = packed;
+    } else {
+      float* rec = a.partials + (long long)item * a.item_stride;
+      *(float4v*)(rec + gg * kHeadDim + d4) = o;
+      if (d4 == 0) {
+        rec[G * kHeadDim + gg] = M;
+        rec[G * kHeadDim + G + gg] = Ls;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------- combine kernel
+__device__ __forceinline__ float block_max(float v, float* red, int tid) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < kCombineThreads / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red, int tid) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < kCombineThreads / 64; ++w) r += red[w];
+  return r;
+}
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
+  __shared__ float s_w[kMaxItemsPerHead];
+  __shared__ float s_red[kCombineThreads / 64];
+  __shared__ float4v s_acc[kCombineThreads];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int Hq = a.num_kv_heads * a.group;
+  constexpr int kChunks = kHeadDim / kCombineDChunk;
+  const int blk = blockIdx.x;
+  const int dc = blk % kChunks;
+  const int hq = (blk / kChunks) % Hq;
+  const int b = blk / (kChunks * Hq);
+
+  const Totals tt = plan_totals(a.context_lens, a.batch, a.max_tokens, lane);
+  const int S = split_tokens(tt.n_tot, tt.active, a.per_head);
+  const int n = clamp_len(a.context_lens[b], a.max_tokens);
+  uint16_t* orow = a.out + ((long long)b * Hq + hq) * kHeadDim + dc * kCombineDChunk;
+  if (n == 0) {
+    if (tid < kCombineDChunk) orow[tid] = 0;
+    return;
+  }
+  int nsb, first;
+  plan_row(a.context_lens, a.batch, a.max_tokens, S, b, lane, nsb, first);
+  if (nsb <= 1) return;   // written by the split kernel
+
+  const int h = hq / a.group;
+  const int g = hq % a.group;
+  const int mo = a.group * kHeadDim;
+  auto rec = [&](int s) {
+    return a.partials + (long long)((first + s) * a.num_kv_heads + h) * a.item_stride;
+  };
+
+  float mx = -INFINITY;
+  for (int s = tid; s < nsb; s += kCombineThreads) mx = fmaxf(mx, rec(s)[mo + g]);
+  const float M = block_max(mx, s_red, tid);
+
+  float lsum = 0.f;
+  for (int s = tid; s < nsb; s += kCombineThreads) {
+    const float w = exp2_fast(rec(s)[mo + g] - M);
+    s_w[s] = w;
+    lsum += w * rec(s)[mo + a.group + g];
+  }
+  const float L = block_sum(lsum, s_red, tid);   // ends with a barrier: s_w is visible
+
+  const int d4 = tid & 7;
+  const int sl = tid >> 3;
+  float4v acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = sl; s < nsb; s += kCombineThreads / 8) {
+    acc += s_w[s] * *(const float4v*)(rec(s) + g * kHeadDim + dc * kCombineDChunk + d4 * 4);
+  }
+  s_acc[tid] = acc;
+  __syncthreads();
+  for (int off = kCombineThreads / 16; off > 0; off >>= 1) {
+    if (sl < off) s_acc[tid] += s_acc[tid + off * 8];
+    __syncthreads();
+  }
+  if (tid < 8) {
+    const float inv = 1.0f / L;
+    const float4v o = s_acc[tid];
+    uint2 packed;
+    packed.x = pack_half2(o[0] * inv, o[1] * inv);
+    packed.y = pack_half2(o[2] * inv, o[3] * inv);
+    *(uint2*)(orow + tid * 4) = packed;
+  }
+}
+
+// ------------------------------------------------------------ widen (test)
+// Each thread widens one group of four codes with the same helpers the K
+// path uses, so every byte position of both selectors is exercised.
+__global__ void widen_kernel(const uint8_t* in, uint16_t* out16, float* out32, long long n) {
+  const long long grp = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long i0 = grp * 4;
+  if (i0 >= n) return;
+  uint32_t x = 0;
+  for (int k = 0; k < 4; ++k) {
+    if (i0 + k < n) x |= (uint32_t)in[i0 + k] << (8 * k);
+  }
+  const uint32_t lo = widen_lo(x), hi = widen_hi(x);
+  const uint16_t bits[4] = {(uint16_t)(lo & 0xFFFFu), (uint16_t)(lo >> 16), (uint16_t)(hi & 0xFFFFu),
+                            (uint16_t)(hi >> 16)};
+  for (int k = 0; k < 4; ++k) {
+    if (i0 + k >= n) break;
+    if (out16) out16[i0 + k] = bits[k];
+    if (out32) out32[i0 + k] = (float)__builtin_bit_cast(_Float16, bits[k]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attend(const AttendArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  const int grid = a.batch * a.num_kv_heads * a.group * (kHeadDim / kCombineDChunk);
+  hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kCombineThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_widen(const uint8_t* in, uint16_t* out_f16, float* out_f32, int64_t n,
+                        hipStream_t stream) {
+  const long long groups = (n + 3) / 4;
+  const int threads = 256;
+  const long long blocks = (groups + threads - 1) / threads;
+  hipLaunchKernelGGL(widen_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, in, out_f16,
+                     out_f32, (long long)n);
+  return hipGetLastError();
+}
+
+hipError_t attend_blocks_per_cu(int* blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, attend_kernel, kThreads, 0);
+}
+
+}  // namespace xqa

@@ -1,0 +1,147 @@
+/*
+ * xqa.h -- batched grouped-query decode attention over a paged FP8-E5M2 KV
+ * cache, for one AMD Instinct MI355X (gfx950) GPU.
+ *
+ * The operation (page "[Kernel][SM70] Pipeline batched E5M2 XQA decode",
+ * sections Purpose and Starting bottleneck: batched long-context XQA decode
+ * with an FP8 E5M2 KV cache; section Pending work and gates: randomized
+ * physical pages, ragged and boundary context lengths). For every sequence b
+ * in [0, batch) and query head hq in [0, Hq), with G = Hq / Hkv:
+ *
+ *     h = hq / G                     (query heads h*G .. h*G+G-1 share KV head h)
+ *     n = min(context_lens[b], max_pages_per_seq * page_size)
+ *     token t < n lives in page block_table[b][t / page_size], slot t % page_size
+ *     z_t = scale * sum_d q[b][hq][d] * dec(k[page][h][slot][d])
+ *     out[b][hq][:] = sum_t softmax(z)_t * dec(v[page][h][slot][:])
+ *     n <= 0 gives a zero row.
+ *
+ * dec() is the OCP E5M2 decode: every code widens exactly to binary16 (the
+ * code is the high byte of the binary16 word). Scores, softmax and the
+ * weighted sum are accumulated in fp32; out is binary16, round to nearest even.
+ *
+ * Data layout (all device memory, owned by the caller):
+ *     q            binary16 [batch][Hq][head_dim], contiguous
+ *     k_pages      uint8    [num_pages][Hkv][page_size][head_dim] E5M2 codes
+ *     v_pages      uint8    same layout as k_pages
+ *     block_table  int32    [batch][max_pages_per_seq], row stride max_pages_per_seq
+ *     context_lens int32    [batch]
+ *     out          binary16 [batch][Hq][head_dim], contiguous
+ * Supported shapes: head_dim 128, page_size 16, 1 <= G <= 16.
+ *
+ * Device-resident values are not validated (that would need a device->host
+ * copy and would break graph capture). Contract: block-table entries that a
+ * sequence's first ceil(n / page_size) pages use must be valid page ids;
+ * entries past them are never read; slots >= n of the last page and pages not
+ * referenced never influence out, whatever their bytes (NaN codes included);
+ * block tables may alias pages across sequences (read-only sharing).
+ *
+ * Errors are fail-closed: on any non-XQA_OK status nothing was launched.
+ * Streams are passed as void* and must be a hipStream_t (0 = null stream).
+ * All entry points are thread-safe except that one handle serves one stream
+ * at a time: its workspace is shared between the calls made with it.
+ */
+#ifndef XQA_H
+#define XQA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct xqa_handle_s* xqa_handle_t;
+
+typedef enum {
+  XQA_OK = 0,
+  XQA_ERR_INVALID_ARG = 1,   /* null / misaligned pointer, out-of-range scalar        */
+  XQA_ERR_UNSUPPORTED = 2,   /* shape outside the supported set                       */
+  XQA_ERR_OUT_OF_MEMORY = 3, /* workspace allocation failed (xqa_create only)         */
+  XQA_ERR_HIP = 4            /* HIP runtime error (no device, launch failure, ...)    */
+} xqa_status_t;
+
+typedef struct {
+  int32_t max_batch;         /* >= 1: largest batch a decode call may pass              */
+  int32_t num_q_heads;       /* Hq, multiple of num_kv_heads                            */
+  int32_t num_kv_heads;      /* Hkv >= 1                                                */
+  int32_t head_dim;          /* 128                                                     */
+  int32_t page_size;         /* 16                                                      */
+  int32_t max_pages_per_seq; /* >= 1: block-table row stride in int32 elements          */
+  int32_t max_work_items;    /* 0: sized from the device's occupancy; else the split    */
+                             /* workgroup count (>= Hkv * (max_batch + 1))              */
+} xqa_config_t;
+
+typedef struct {
+  int32_t device;            /* HIP device the handle was created on                    */
+  int32_t max_work_items;    /* grid of the split kernel                                */
+  int32_t items_per_head;    /* max_work_items / Hkv: bound on splits per sequence      */
+  int32_t token_granule;     /* split lengths are multiples of this many tokens         */
+  int32_t threads_per_item;  /* workgroup size of the split kernel                      */
+  int32_t item_stride_floats;/* floats per partial record in the workspace              */
+  int64_t workspace_bytes;   /* device bytes the handle owns                            */
+} xqa_info_t;
+
+/* Create a handle on the current HIP device. Validates cfg, sizes the split
+ * grid from the split kernel's occupancy and allocates the partial-result
+ * workspace (the only allocation the library makes). *out_handle is set only
+ * on XQA_OK. Errors: INVALID_ARG (null pointers, non-positive sizes),
+ * UNSUPPORTED (head_dim != 128, page_size != 16, Hq % Hkv != 0, G > 16),
+ * OUT_OF_MEMORY, HIP (no device). */
+xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle);
+
+/* Free the handle and its workspace. NULL is a no-op. The caller must make
+ * sure no work issued with the handle is still running. */
+xqa_status_t xqa_destroy(xqa_handle_t handle);
+
+/* Copy the handle's sizes into *info. */
+xqa_status_t xqa_get_info(xqa_handle_t handle, xqa_info_t* info);
+
+/* One decode step: the split kernel and the combine kernel, back to back on
+ * `stream`. Nothing is allocated and nothing waits on the host, so the call
+ * can be captured into a HIP graph and replayed with new contents of q,
+ * block_table and context_lens. batch must be in [1, max_batch]; scale must
+ * be finite. q, k_pages, v_pages and out must be 16-byte aligned,
+ * block_table and context_lens 4-byte aligned. The calling thread's current
+ * device must be the handle's device. Errors: INVALID_ARG, HIP. */
+xqa_status_t xqa_decode(xqa_handle_t handle, const void* q, const uint8_t* k_pages,
+                        const uint8_t* v_pages, const int32_t* block_table,
+                        const int32_t* context_lens, int32_t batch, float scale,
+                        void* out, void* stream);
+
+/* First stage of xqa_decode: plan, gather, widen, QK, online softmax, PV.
+ * Rows whose sequence fits one work item are written to out directly; the
+ * others leave per-item partial states in the workspace for
+ * xqa_decode_combine, which must follow on the same stream with the same
+ * context_lens, batch and out before the handle is used again. */
+xqa_status_t xqa_decode_attend(xqa_handle_t handle, const void* q, const uint8_t* k_pages,
+                               const uint8_t* v_pages, const int32_t* block_table,
+                               const int32_t* context_lens, int32_t batch, float scale,
+                               void* out, void* stream);
+
+/* Second stage: log-sum-exp merge of the partial states of every row that
+ * was split, in a fixed order, plus zero rows for n <= 0. */
+xqa_status_t xqa_decode_combine(xqa_handle_t handle, const int32_t* context_lens,
+                                int32_t batch, void* out, void* stream);
+
+/* Host mirror of the device-side plan, for diagnostics and tests:
+ * context_lens_host is host memory [batch]. Writes the split length in
+ * tokens and the number of split work items the device would use. */
+xqa_status_t xqa_plan(xqa_handle_t handle, const int32_t* context_lens_host, int32_t batch,
+                      int32_t* split_tokens, int32_t* num_items);
+
+/* Test hook: widen n E5M2 codes with the same device routine the split
+ * kernel uses for K. out_f16 receives the binary16 bit patterns, out_f32 the
+ * same values as fp32 (either output may be NULL). Device pointers. */
+xqa_status_t xqa_debug_widen_e5m2(const uint8_t* in, uint16_t* out_f16, float* out_f32,
+                                  int64_t n, void* stream);
+
+/* Static name of a status code. */
+const char* xqa_status_string(xqa_status_t status);
+
+/* Human-readable detail of the calling thread's most recent error. */
+const char* xqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XQA_H */

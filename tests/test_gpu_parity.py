@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Element-wise comparison under the stated tolerance (2e-3 absolute or 1e-2
+relative) plus a relative-L2 gate, on seeded inputs; exact checks where the
+arithmetic makes the result exact; bitwise invariances (repeat, stage split,
+page permutation).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests._helpers import assert_parity, compare, ensure_library
+from workloads import make_config, make_custom
+from workloads.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_library()
+
+
+def Xqa(**kw):
+    from decode_attention_paged_e5m2_amd import Xqa as X
+    return X(**kw)
+
+
+def run(w, xqa=None, dev=None, **over):
+    if dev is None:
+        dev = to_device(w)
+    if xqa is None:
+        xqa = Xqa(max_batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                  max_pages_per_seq=w.max_pages_per_seq)
+    args = dict(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages, block_table=dev.block_table,
+                context_lens=dev.context_lens, scale=w.scale)
+    args.update(over)
+    out = xqa.decode(**args)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), xqa, dev
+
+
+def reference(w):
+    kp, vp = w.pools()
+    return oracle.decode_attention(w.q, kp, vp, w.block_table, w.context_lens, w.scale)
+
+
+def log(label, st):
+    print(f"[parity] {label}: max_abs={st['max_abs']:.3e} max_rel={st['max_rel']:.3e} "
+          f"rel_l2={st['rel_l2']:.3e} n={st['n']}", flush=True)
+
+
+# ------------------------------------------------------------- widening
+
+def test_widen_all_256_codes_bit_exact():
+    from decode_attention_paged_e5m2_amd import debug_widen_e5m2
+    for n in (256, 1001):   # 1001: a ragged tail of the 4-code groups
+        codes = np.arange(n, dtype=np.int64) % 256
+        codes = ((codes * 77 + 5) % 256 if n != 256 else codes).astype(np.uint8)
+        bits, vals = debug_widen_e5m2(torch.from_numpy(codes).cuda())
+        bits = bits.cpu().numpy().view(np.uint16)
+        vals = vals.cpu().numpy().astype(np.float64)
+        assert (bits == codes.astype(np.uint16) << 8).all()
+        ref = oracle.decode_e5m2(codes)
+        nan = np.isnan(ref)
+        assert (np.isnan(vals) == nan).all()
+        assert (vals[~nan] == ref[~nan]).all()
+        assert (np.signbit(vals[~nan]) == np.signbit(ref[~nan])).all()
+
+
+# ---------------------------------------------------------- small parity
+
+def test_config1_tiny():
+    w = make_config(1)
+    out, _, _ = run(w)
+    st = assert_parity(out, reference(w), "cfg1")
+    log("cfg1", st)
+
+
+def test_config2_uniform_short():
+    w = make_config(2)
+    out, _, _ = run(w)
+    st = assert_parity(out, reference(w), "cfg2")
+    log("cfg2", st)
+
+
+@pytest.mark.parametrize("hkv,hq", [(1, 8), (2, 16), (4, 32), (2, 4), (1, 16), (3, 3)])
+def test_context_sweep_1_to_64(hkv, hq):
+    ctx = list(range(1, 65))
+    w = make_custom(ctx, hkv, hq, [7, hkv, hq], pool_pages=300)
+    out, _, _ = run(w)
+    st = assert_parity(out, reference(w), f"sweep hkv={hkv} hq={hq}")
+    log(f"sweep hkv={hkv} hq={hq}", st)
+
+
+def test_split_boundaries():
+    # Lengths on both sides of the split length S the plan picks, and of the
+    # 32-token block and 128-token granule inside an item.
+    probe = Xqa(max_batch=12, num_q_heads=16, num_kv_heads=2, max_pages_per_seq=512)
+    base = [4000, 4000, 4000, 4000, 4000, 4000]
+    S, _ = probe.plan(base + [1] * 6)
+    ctx = base + [S - 1, S, S + 1, 2 * S + 31, 2 * S + 32, 2 * S + 33]
+    S2, items = probe.plan(ctx)
+    w = make_custom(ctx, 2, 16, 42, pool_pages=12 * 512, max_pages_per_seq=512)
+    out, _, _ = run(w, xqa=probe)
+    st = assert_parity(out, reference(w), f"split boundaries S={S2} items={items}")
+    log(f"boundaries S={S2} items={items}", st)
+
+
+def test_zero_and_negative_lengths_and_clamp():
+    # Sequence 3 fills its three pages; a length beyond the block table's
+    # capacity clamps to 3 * 16 = 48 tokens.
+    w = make_custom([0, 5, 40, 48], 2, 16, 43, pool_pages=10, max_pages_per_seq=3)
+    dev = to_device(w)
+    lens = dev.context_lens.clone()
+    lens[0] = -7
+    lens[3] = 100000
+    out, _, _ = run(w, dev=dev, context_lens=lens)
+    kp, vp = w.pools()
+    ref = oracle.decode_attention(w.q, kp, vp, w.block_table, lens.cpu().numpy(), w.scale)
+    assert (out[0] == 0).all()
+    assert np.isfinite(out).all()
+    assert_parity(out, ref, "zero/negative/clamp")
+
+
+def test_single_token_is_exact_and_constant_v_is_exact():
+    w = make_custom([1, 1, 1, 1], 2, 16, 44)
+    out, _, _ = run(w)
+    ref = reference(w)
+    assert (out == ref.astype(np.float16).astype(np.float32)).all()
+    w2 = make_custom([3, 100, 1000, 2049], 2, 16, 45)
+    for b in range(w2.batch):
+        w2.v_tokens[b][:] = 0x45   # 3.0 * 2^1... any finite code
+    out2, _, _ = run(w2)
+    val = oracle.decode_e5m2([0x45])[0]
+    assert (out2 == np.float32(val)).all()
+
+
+def test_scale_zero_gives_mean_of_v():
+    w = make_custom([77, 300], 1, 8, 46)
+    out, _, _ = run(w, scale=0.0)
+    kp, vp = w.pools()
+    ref = oracle.decode_attention(w.q, kp, vp, w.block_table, w.context_lens, 0.0)
+    assert_parity(out, ref, "scale 0")
+
+
+# -------------------------------------------------------------- invariants
+
+def test_repeat_stage_split_and_permutation_bitwise():
+    w = make_custom([3000, 17, 700, 4096, 1], 4, 32, 47, pool_pages=800)
+    out, xqa, dev = run(w)
+    for _ in range(20):
+        again, _, _ = run(w, xqa=xqa, dev=dev)
+        assert (again.view(np.uint32) == out.view(np.uint32)).all()
+    # attend + combine called separately == decode
+    o2 = torch.empty_like(dev.q)
+    xqa.attend(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages, block_table=dev.block_table,
+               context_lens=dev.context_lens, scale=w.scale, out=o2)
+    xqa.combine(context_lens=dev.context_lens, out=o2)
+    torch.cuda.synchronize()
+    assert (o2.float().cpu().numpy() == out).all()
+    # moving every page to another physical slot leaves the result bitwise equal
+    perm = torch.randperm(dev.k_pages.shape[0], generator=torch.Generator().manual_seed(3)).cuda()
+    k2 = torch.empty_like(dev.k_pages)
+    v2 = torch.empty_like(dev.v_pages)
+    k2[perm] = dev.k_pages
+    v2[perm] = dev.v_pages
+    bt2 = perm[dev.block_table.long()].to(torch.int32)
+    o3, _, _ = run(w, xqa=xqa, dev=dev, k_pages=k2, v_pages=v2, block_table=bt2)
+    assert (o3 == out).all()
+
+
+def test_output_canaries_untouched():
+    w = make_custom([100, 2000], 2, 16, 48)
+    dev = to_device(w)
+    xqa = Xqa(max_batch=2, num_q_heads=16, num_kv_heads=2, max_pages_per_seq=w.max_pages_per_seq)
+    buf = torch.full((4, 16, 128), float("nan"), dtype=torch.float16, device="cuda")
+    out = buf[1:3]
+    xqa.decode(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages, block_table=dev.block_table,
+               context_lens=dev.context_lens, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[0]).all() and torch.isnan(buf[3]).all()
+    assert_parity(out.float().cpu().numpy(), reference(w), "canaries")
+
+
+def test_aliased_pages_across_sequences():
+    # Two sequences sharing their prefix pages (read-only aliasing).
+    w = make_custom([500, 500], 1, 8, 49, pool_pages=64)
+    w.block_table[1, :20] = w.block_table[0, :20]
+    w.k_tokens[1][:320] = w.k_tokens[0][:320]
+    w.v_tokens[1][:320] = w.v_tokens[0][:320]
+    out, _, _ = run(w)
+    assert_parity(out, reference(w), "aliased")
+
+
+def test_bad_arguments_raise():
+    from decode_attention_paged_e5m2_amd import XqaError
+    w = make_config(1)
+    dev = to_device(w)
+    xqa = Xqa(max_batch=1, num_q_heads=8, num_kv_heads=1, max_pages_per_seq=16)
+    with pytest.raises(ValueError):
+        xqa.decode(q=dev.q.float(), k_pages=dev.k_pages, v_pages=dev.v_pages,
+                   block_table=dev.block_table, context_lens=dev.context_lens, scale=0.1)
+    with pytest.raises(ValueError):
+        xqa.decode(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages,
+                   block_table=dev.block_table, context_lens=dev.context_lens, scale=float("inf"))
+    import ctypes
+    from decode_attention_paged_e5m2_amd import _lib
+    lib = _lib.load()
+    st = lib.xqa_decode(xqa._h, ctypes.c_void_p(dev.q.data_ptr() + 2), ctypes.c_void_p(dev.k_pages.data_ptr()),
+                        ctypes.c_void_p(dev.v_pages.data_ptr()), ctypes.c_void_p(dev.block_table.data_ptr()),
+                        ctypes.c_void_p(dev.context_lens.data_ptr()), 1, ctypes.c_float(0.1),
+                        ctypes.c_void_p(dev.q.data_ptr()), None)
+    assert st == 1
+    st = lib.xqa_decode(xqa._h, ctypes.c_void_p(dev.q.data_ptr()), ctypes.c_void_p(dev.k_pages.data_ptr()),
+                        ctypes.c_void_p(dev.v_pages.data_ptr()), ctypes.c_void_p(dev.block_table.data_ptr()),
+                        ctypes.c_void_p(dev.context_lens.data_ptr()), 2, ctypes.c_float(0.1),
+                        ctypes.c_void_p(dev.q.data_ptr()), None)
+    assert st == 1
+
+
+# ------------------------------------------------------------ full configs
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_full_size_configs(idx):
+    w = make_config(idx)
+    print(f"[parity] cfg{idx}: generating done, Σctx={w.total_tokens}", flush=True)
+    out, xqa, _ = run(w)
+    st = assert_parity(out, reference(w), f"cfg{idx}")
+    S, items = xqa.plan(w.context_lens)
+    log(f"cfg{idx} S={S} items={items}", st)
