@@ -13,7 +13,7 @@ XQA_ERR_OUT_OF_MEMORY = 3
 XQA_ERR_HIP = 4
 
 EXPORTED = [
-    "xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_attend",
+    "xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_split",
     "xqa_decode_combine", "xqa_plan", "xqa_debug_widen_e5m2", "xqa_status_string",
     "xqa_last_error",
 ]
@@ -68,7 +68,7 @@ def load() -> ctypes.CDLL:
     lib.xqa_get_info.argtypes = [vp, ctypes.POINTER(XqaInfo)]
     dec = [vp, vp, vp, vp, vp, vp, i32, f32, vp, vp]
     lib.xqa_decode.argtypes = dec
-    lib.xqa_decode_attend.argtypes = dec
+    lib.xqa_decode_split.argtypes = dec
     lib.xqa_decode_combine.argtypes = [vp, vp, i32, vp, vp]
     lib.xqa_plan.argtypes = [vp, ctypes.POINTER(i32), i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.xqa_debug_widen_e5m2.argtypes = [vp, vp, vp, i64, vp]
@@ -76,7 +76,7 @@ def load() -> ctypes.CDLL:
     lib.xqa_status_string.restype = ctypes.c_char_p
     lib.xqa_last_error.argtypes = []
     lib.xqa_last_error.restype = ctypes.c_char_p
-    for name in ("xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_attend",
+    for name in ("xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_split",
                  "xqa_decode_combine", "xqa_plan", "xqa_debug_widen_e5m2"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib

@@ -117,28 +117,31 @@ class Xqa:
                block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                out: Optional[torch.Tensor] = None, batch: Optional[int] = None,
                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-        """One decode step (split + combine kernels) on the current stream."""
+        """One decode step (split kernel + combine kernel) on the current stream."""
         out, args = self._args(q, k_pages, v_pages, block_table, context_lens, out, batch, scale, stream)
         _lib.check(_lib.load().xqa_decode(*args))
         return out
 
-    def attend(self, *, q, k_pages, v_pages, block_table, context_lens, scale, out=None,
-               batch=None, stream=None) -> torch.Tensor:
-        """First stage only (see xqa_decode_attend); combine() must follow."""
+    def split(self, *, q, k_pages, v_pages, block_table, context_lens, scale, out=None,
+              batch=None, stream=None) -> torch.Tensor:
+        """First stage only (xqa_decode_split); combine() must follow."""
         out, args = self._args(q, k_pages, v_pages, block_table, context_lens, out, batch, scale, stream)
-        _lib.check(_lib.load().xqa_decode_attend(*args))
+        _lib.check(_lib.load().xqa_decode_split(*args))
         return out
 
     def combine(self, *, context_lens, out, batch=None, stream=None) -> torch.Tensor:
-        """Second stage only (see xqa_decode_combine)."""
+        """Second stage only (xqa_decode_combine)."""
         if batch is None:
             batch = out.shape[0]
-        _need(context_lens.dtype == torch.int32 and context_lens.device == self.device,
-              "context_lens must be int32 on the handle's device")
-        _need(out.dtype == torch.float16 and out.device == self.device and out.is_contiguous(),
+        _need(isinstance(context_lens, torch.Tensor) and context_lens.dtype == torch.int32
+              and context_lens.device == self.device and context_lens.is_contiguous(),
+              "context_lens must be contiguous int32 on the handle's device")
+        _need(isinstance(out, torch.Tensor) and out.dtype == torch.float16
+              and out.device == self.device and out.is_contiguous(),
               "out must be contiguous float16 on the handle's device")
         _need(out.dim() == 3 and out.shape[1:] == (self.num_q_heads, self.head_dim)
-              and out.shape[0] >= batch and context_lens.shape[0] >= batch, "bad shapes")
+              and out.shape[0] >= batch and context_lens.shape[0] >= batch
+              and 1 <= batch <= self.max_batch, "bad shapes or batch")
         _lib.check(_lib.load().xqa_decode_combine(self._h, _ptr(context_lens), int(batch), _ptr(out),
                                                   _stream_ptr(stream, self.device)))
         return out

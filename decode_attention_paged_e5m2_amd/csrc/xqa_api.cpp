@@ -19,7 +19,7 @@ struct xqa_handle_s {
   int grid;          // split workgroups = work-item capacity
   int per_head;      // grid / Hkv
   int item_stride;   // floats per partial record
-  float* partials;
+  float* partials;   // workspace: grid partial records
   size_t workspace_bytes;
 };
 
@@ -89,21 +89,6 @@ xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_page
   a.item_stride = h->item_stride;
   a.scale_log2e = scale * 1.4426950408889634f;
   return a;
-}
-
-xqa::CombineArgs combine_args(xqa_handle_t h, const int32_t* context_lens, int32_t batch,
-                              void* out) {
-  xqa::CombineArgs c;
-  c.context_lens = context_lens;
-  c.partials = h->partials;
-  c.out = static_cast<uint16_t*>(out);
-  c.batch = batch;
-  c.num_kv_heads = h->cfg.num_kv_heads;
-  c.group = h->cfg.num_q_heads / h->cfg.num_kv_heads;
-  c.max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
-  c.per_head = h->per_head;
-  c.item_stride = h->item_stride;
-  return c;
 }
 
 }  // namespace
@@ -183,6 +168,7 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
     if (e == hipErrorOutOfMemory) return fail(XQA_ERR_OUT_OF_MEMORY, "workspace allocation failed");
     return hip_fail(e, "hipMalloc");
   }
+
   *out_handle = h;
   return XQA_OK;
 }
@@ -208,17 +194,17 @@ xqa_status_t xqa_get_info(xqa_handle_t h, xqa_info_t* info) {
   return XQA_OK;
 }
 
-xqa_status_t xqa_decode_attend(xqa_handle_t h, const void* q, const uint8_t* k_pages,
-                               const uint8_t* v_pages, const int32_t* block_table,
-                               const int32_t* context_lens, int32_t batch, float scale,
-                               void* out, void* stream) {
+xqa_status_t xqa_decode_split(xqa_handle_t h, const void* q, const uint8_t* k_pages,
+                              const uint8_t* v_pages, const int32_t* block_table,
+                              const int32_t* context_lens, int32_t batch, float scale, void* out,
+                              void* stream) {
   xqa_status_t st =
       check_decode_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
   if (st != XQA_OK) return st;
   if ((st = check_device(h)) != XQA_OK) return st;
   const xqa::AttendArgs a =
       attend_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
-  hipError_t e = xqa::launch_attend(a, h->grid, static_cast<hipStream_t>(stream));
+  hipError_t e = xqa::launch_split(a, h->grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
   return XQA_OK;
 }
@@ -233,8 +219,9 @@ xqa_status_t xqa_decode_combine(xqa_handle_t h, const int32_t* context_lens, int
     return fail(XQA_ERR_INVALID_ARG, "batch outside [1, max_batch]");
   xqa_status_t st = check_device(h);
   if (st != XQA_OK) return st;
-  const xqa::CombineArgs c = combine_args(h, context_lens, batch, out);
-  hipError_t e = xqa::launch_combine(c, static_cast<hipStream_t>(stream));
+  xqa::AttendArgs a = attend_args(h, nullptr, nullptr, nullptr, nullptr, context_lens, batch, 0.f,
+                                  out);
+  hipError_t e = xqa::launch_combine(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return XQA_OK;
 }
@@ -250,9 +237,9 @@ xqa_status_t xqa_decode(xqa_handle_t h, const void* q, const uint8_t* k_pages,
   const xqa::AttendArgs a =
       attend_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = xqa::launch_attend(a, h->grid, s);
+  hipError_t e = xqa::launch_split(a, h->grid, s);
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
-  e = xqa::launch_combine(combine_args(h, context_lens, batch, out), s);
+  e = xqa::launch_combine(a, s);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return XQA_OK;
 }

@@ -17,10 +17,12 @@ constexpr int kGranule = kWaves * kBlockTokens;        // split lengths are mult
 constexpr int kMaxItemsPerHead = 2048;                 // bound on splits per sequence
 constexpr int kCombineThreads = 256;
 constexpr int kCombineDChunk = 32;                     // head-dim columns per combine workgroup
+constexpr int kCombineSplitLanes = 32;                 // split lanes per combine workgroup
+constexpr int kCombinePerLane = 4;                     // split states a lane keeps in registers
 
 // ---------------------------------------------------------------------------
-// The split plan. Every split workgroup and every combine workgroup evaluates
-// it on the device from context_lens alone, so the grid never depends on
+// The split plan. Every workgroup of both kernels evaluates it on the device
+// from context_lens alone, so the grid never depends on
 // device data and a captured graph replays exactly with new lengths.
 //
 //   n_b    = clamp(context_lens[b], 0, max_tokens)
@@ -57,7 +59,7 @@ struct AttendArgs {
   const int32_t* block_table;
   const int32_t* context_lens;
   uint16_t* out;
-  float* partials;
+  float* partials;        // [grid][item_stride] split states
   int32_t batch;
   int32_t num_kv_heads;
   int32_t group;
@@ -68,20 +70,8 @@ struct AttendArgs {
   float scale_log2e;      // scale * log2(e): scores are kept in base-2 units
 };
 
-struct CombineArgs {
-  const int32_t* context_lens;
-  const float* partials;
-  uint16_t* out;
-  int32_t batch;
-  int32_t num_kv_heads;
-  int32_t group;
-  int32_t max_tokens;
-  int32_t per_head;
-  int32_t item_stride;
-};
-
-hipError_t launch_attend(const AttendArgs& a, int grid, hipStream_t stream);
-hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream);
+hipError_t launch_combine(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_widen(const uint8_t* in, uint16_t* out_f16, float* out_f32, int64_t n,
                         hipStream_t stream);
 hipError_t attend_blocks_per_cu(int* blocks);

@@ -7,14 +7,21 @@
 // + conversion, PV, synchronisation -- map onto the code below; the tiling
 // is designed for CDNA4 (64-wide waves, MFMA, DPP) rather than taken from it.
 //
-// Split kernel (one workgroup = one work item = (sequence, KV head, token
-// range); four waves take interleaved 32-token blocks = 2 pages):
+// A decode step is two kernels. In the split kernel each workgroup is one
+// work item = (sequence, KV head, token range); its four waves take
+// interleaved 32-token blocks (2 pages):
 //
+//   Plan: every workgroup derives the split length and its own item from
+//      context_lens (O(batch) integer work), so the grid is fixed and a
+//      captured graph replays exactly with new lengths.
+//   Gather: a wave fetches the page ids of its next 32 blocks with one
+//      vector load and reads them out with v_readlane; K and V of a block are
+//      eight 16-byte loads per lane, issued one block ahead (ping-pong).
 //   K: lane l reads token l%16 of the page, head-dim bytes
-//      [16q, 16q+16) and [64+16q, 64+16q+16) (q = l/16): two 16-byte loads
-//      per page, each instruction covering 64 contiguous bytes of all 16
-//      token rows. Widening is one v_perm_b32 per two codes (the E5M2 code is
-//      the high byte of its binary16 value).
+//      [16q, 16q+16) and [64+16q, 64+16q+16) (q = l/16): each load
+//      instruction covers 64 contiguous bytes of all 16 token rows.
+//      Widening is one v_perm_b32 per two codes (the E5M2 code is the high
+//      byte of its binary16 value).
 //   QK: S^T = K . Q^T with v_mfma_f32_16x16x32_f16, M = the 16 tokens of a
 //      page, N = the query heads of the group (padded to 16), four MFMAs
 //      over head_dim 128. The contraction index may be permuted freely as
@@ -30,16 +37,21 @@
 //      contraction axis (tokens) is strided in memory, so each quad of lanes
 //      loads four token rows and transposes the 4x4 byte tile with two DPP
 //      quad permutes and three v_perm_b32, the last two of which also widen
-//      the bytes to binary16.
-//   The four waves' (max, sum, O) states merge in LDS; a sequence that fits
-//   one item is normalised and written directly, otherwise the item's state
-//   goes to the workspace and the combine kernel merges the splits.
+//      the bytes to binary16. Row sums come from one more MFMA with an
+//      all-ones A operand.
+//   Merge: the four waves' (max, sum, O) states merge in LDS. A sequence
+//      that fits one item is normalised and written directly; otherwise the
+//      item stores its state in the workspace.
 //
-// Combine kernel: per (sequence, query head, 32-column chunk), the exact
-// log-sum-exp merge M = max m_s, L = sum l_s 2^(m_s-M),
-// out = sum 2^(m_s-M) O_s / L in a fixed order, so results are bitwise
-// reproducible run to run, between eager calls and graph replays, and under
-// any permutation of the physical pages.
+// The combine kernel then merges the states of every split sequence with
+// the exact log-sum-exp rule M = max m_s, L = sum l_s 2^(m_s-M),
+// out = sum 2^(m_s-M) O_s / L, and writes the zero rows of empty sequences.
+// The kernel boundary makes the split states visible across the chip's
+// separately cached dies without any in-kernel cache write-back.
+//
+// Every reduction runs in a fixed order, so results are bitwise reproducible
+// run to run, between eager calls and graph replays, and under any
+// permutation of the physical pages.
 
 #include <math.h>
 
@@ -272,27 +284,33 @@ __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4],
   }
 }
 
-__global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_l[kWaves][kMaxGroup];
   __shared__ float s_o[kWaves][kMaxGroup][kHeadDim + 4];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int G = a.group;
+  const int Hkv = a.num_kv_heads;
+  const int item = blockIdx.x;
 
   const Totals tt = plan_totals(a.context_lens, a.batch, a.max_tokens, lane);
-  const int S = split_tokens(tt.n_tot, tt.active, a.per_head);
-  const int item = blockIdx.x;
-  const int h = item % a.num_kv_heads;
+  const int S = uniform(split_tokens(tt.n_tot, tt.active, a.per_head));
+
+  const int h = item % Hkv;
   int b, s, nsb;
-  if (!plan_locate(a.context_lens, a.batch, a.max_tokens, S, item / a.num_kv_heads, lane, b, s,
-                   nsb)) {
+  if (!plan_locate(a.context_lens, a.batch, a.max_tokens, S, item / Hkv, lane, b, s, nsb)) {
     return;   // beyond the planned items: the whole workgroup leaves
   }
-  const int n = clamp_len(a.context_lens[b], a.max_tokens);
+  b = uniform(b);
+  s = uniform(s);
+  nsb = uniform(nsb);
+  const int n = uniform(clamp_len(a.context_lens[b], a.max_tokens));
   const int t_begin = s * S;
   const int t_end = min(n, t_begin + S);
-  const int G = a.group;
   const int g = lane & 15;
   const int q = lane >> 4;
 
@@ -300,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   // head-dim values 64*(i/2) + 16q + 8*(i%2) + 0..7, matching the K bytes.
   half8 qf[4];
   if (g < G) {
-    const uint16_t* qrow = a.q + ((long long)b * a.num_kv_heads * G + (long long)h * G + g) * kHeadDim;
+    const uint16_t* qrow = a.q + ((long long)b * Hkv * G + (long long)h * G + g) * kHeadDim;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       qf[i] = *(const half8*)(qrow + 64 * (i >> 1) + 16 * q + 8 * (i & 1));
@@ -323,32 +341,47 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   for (int t = 0; t < 8; ++t) st.o[t] = float4v{0.f, 0.f, 0.f, 0.f};
 
   const int32_t* bt = a.block_table + (long long)b * a.max_pages;
-  const size_t page_stride = (size_t)a.num_kv_heads * kPageHeadBytes;
-  const size_t head_off = (size_t)h * kPageHeadBytes;
+  const size_t page_stride = (size_t)Hkv * kPageHeadBytes;
+  const uint8_t* kbase = a.k_pages + (size_t)h * kPageHeadBytes;
+  const uint8_t* vbase = a.v_pages + (size_t)h * kPageHeadBytes;
   const int nblocks = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
   const int my_blocks = nblocks > wave ? (nblocks - wave + kWaves - 1) / kWaves : 0;
+  const int first_page = t_begin >> 4;
+  const int last_page = (t_end - 1) >> 4;
 
-  if (my_blocks > 0) {
-    auto load = [&](RawBlock& r, int j) {
-      const int tok0 = t_begin + j * kBlockTokens;
-      const int pa = bt[tok0 >> 4];
-      const int pb = (tok0 + kPageSize < t_end) ? bt[(tok0 >> 4) + 1] : pa;
-      const size_t oa = (size_t)pa * page_stride + head_off;
-      const size_t ob = (size_t)pb * page_stride + head_off;
-      load_block(r, a.k_pages + oa, a.k_pages + ob, a.v_pages + oa, a.v_pages + ob, koff, voff);
+  // The wave's blocks are j = wave + 4m. Page ids are fetched 32 blocks at a
+  // time with one vector load (lane i: block m = i/2, page (i&1)) and read
+  // out with v_readlane, so address generation never waits on a scalar miss.
+  for (int c0 = 0; c0 < my_blocks; c0 += 32) {
+    int pg = first_page + 2 * (wave + kWaves * (c0 + (lane >> 1))) + (lane & 1);
+    pg = min(pg, last_page);   // blocks past the end read a valid page; masked later
+    const int ids = bt[pg];
+    const int cnt = min(32, my_blocks - c0);
+
+    auto issue = [&](RawBlock& r, int mm) {
+      const int pa = __builtin_amdgcn_readlane(ids, 2 * mm);
+      const int pb = __builtin_amdgcn_readlane(ids, 2 * mm + 1);
+      load_block(r, kbase + (size_t)pa * page_stride, kbase + (size_t)pb * page_stride,
+                 vbase + (size_t)pa * page_stride, vbase + (size_t)pb * page_stride, koff, voff);
     };
-    RawBlock cur, nxt;
-    int j = wave;
-    load(cur, j);
-    for (int it = 0; it + 1 < my_blocks; ++it) {
-      load(nxt, j + kWaves);
-      process_block<false>(cur, qf, st, a.scale_log2e, t_begin + j * kBlockTokens, t_end, lane,
-                           sel1, selh0, selh1);
-      cur = nxt;
-      j += kWaves;
+    auto tok0 = [&](int mm) { return t_begin + (wave + kWaves * (c0 + mm)) * kBlockTokens; };
+
+    RawBlock A, B;
+    issue(A, 0);
+    int mm = 0;
+    for (; mm + 2 < cnt; mm += 2) {
+      issue(B, mm + 1);
+      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
+      issue(A, mm + 2);
+      process_block<false>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
     }
-    process_block<true>(cur, qf, st, a.scale_log2e, t_begin + j * kBlockTokens, t_end, lane, sel1,
-                        selh0, selh1);
+    if (cnt - mm == 2) {
+      issue(B, mm + 1);
+      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
+      process_block<true>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
+    } else {
+      process_block<true>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
+    }
   }
 
   // Publish the wave's state.
@@ -367,7 +400,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   }
   __syncthreads();
 
-  // Merge the four waves (fixed order) and emit the item's result.
+  // Merge the four waves (fixed order): the item's (max, sum, O).
+  uint16_t* out_group = a.out + ((long long)b * Hkv * G + (long long)h * G) * kHeadDim;
+  float* rec = a.partials + (long long)item * a.item_stride;
   for (int e = threadIdx.x; e < G * 32; e += kThreads) {
     const int gg = e >> 5;
     const int d4 = (e & 31) * 4;
@@ -388,10 +423,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
       uint2 packed;
       packed.x = pack_half2(o[0] * inv, o[1] * inv);
       packed.y = pack_half2(o[2] * inv, o[3] * inv);
-      uint16_t* orow = a.out + ((long long)b * a.num_kv_heads * G + (long long)h * G + gg) * kHeadDim;
-      *(uint2*)(orow + d4) = packed;
+      *(uint2*)(out_group + gg * kHeadDim + d4) = packed;
     } else {
-      float* rec = a.partials + (long long)item * a.item_stride;
       *(float4v*)(rec + gg * kHeadDim + d4) = o;
       if (d4 == 0) {
         rec[G * kHeadDim + gg] = M;
@@ -402,34 +435,20 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
 }
 
 // ----------------------------------------------------------- combine kernel
-__device__ __forceinline__ float block_max(float v, float* red, int tid) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  __syncthreads();
-  if ((tid & 63) == 0) red[tid >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < kCombineThreads / 64; ++w) r = fmaxf(r, red[w]);
-  return r;
-}
-
-__device__ __forceinline__ float block_sum(float v, float* red, int tid) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  __syncthreads();
-  if ((tid & 63) == 0) red[tid >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < kCombineThreads / 64; ++w) r += red[w];
-  return r;
-}
-
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
-  __shared__ float s_w[kMaxItemsPerHead];
+// One workgroup per (sequence, query head, 32-column chunk); thread t is
+// split lane t/8 (splits t/8, t/8 + 32, ...) and column lane t%8 (4 columns).
+// Every state a thread needs is loaded in one round, so the kernel costs two
+// dependent memory round trips (lengths, then states) plus LDS reductions.
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) {
   __shared__ float s_red[kCombineThreads / 64];
   __shared__ float4v s_acc[kCombineThreads];
+  __shared__ float s_ls[kCombineThreads];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int Hq = a.num_kv_heads * a.group;
+  const int G = a.group;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = Hkv * G;
   constexpr int kChunks = kHeadDim / kCombineDChunk;
   const int blk = blockIdx.x;
   const int dc = blk % kChunks;
@@ -437,7 +456,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   const int b = blk / (kChunks * Hq);
 
   const Totals tt = plan_totals(a.context_lens, a.batch, a.max_tokens, lane);
-  const int S = split_tokens(tt.n_tot, tt.active, a.per_head);
+  const int S = uniform(split_tokens(tt.n_tot, tt.active, a.per_head));
   const int n = clamp_len(a.context_lens[b], a.max_tokens);
   uint16_t* orow = a.out + ((long long)b * Hq + hq) * kHeadDim + dc * kCombineDChunk;
   if (n == 0) {
@@ -448,43 +467,76 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   plan_row(a.context_lens, a.batch, a.max_tokens, S, b, lane, nsb, first);
   if (nsb <= 1) return;   // written by the split kernel
 
-  const int h = hq / a.group;
-  const int g = hq % a.group;
-  const int mo = a.group * kHeadDim;
+  const int h = hq / G;
+  const int g = hq % G;
+  const int mo = G * kHeadDim;
+  const int col = g * kHeadDim + dc * kCombineDChunk + (tid & 7) * 4;
+  const int sl = tid >> 3;
   auto rec = [&](int s) {
-    return a.partials + (long long)((first + s) * a.num_kv_heads + h) * a.item_stride;
+    return a.partials + ((long long)(first + s) * Hkv + h) * a.item_stride;
   };
 
-  float mx = -INFINITY;
-  for (int s = tid; s < nsb; s += kCombineThreads) mx = fmaxf(mx, rec(s)[mo + g]);
-  const float M = block_max(mx, s_red, tid);
-
-  float lsum = 0.f;
-  for (int s = tid; s < nsb; s += kCombineThreads) {
-    const float w = exp2_fast(rec(s)[mo + g] - M);
-    s_w[s] = w;
-    lsum += w * rec(s)[mo + a.group + g];
+  float mv[kCombinePerLane], lv[kCombinePerLane];
+  float4v ov[kCombinePerLane];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kCombinePerLane; ++k) {
+    const int s = sl + k * kCombineSplitLanes;
+    if (s < nsb) {
+      const float* r = rec(s);
+      mv[k] = r[mo + g];
+      lv[k] = r[mo + G + g];
+      ov[k] = *(const float4v*)(r + col);
+      mloc = fmaxf(mloc, mv[k]);
+    }
   }
-  const float L = block_sum(lsum, s_red, tid);   // ends with a barrier: s_w is visible
-
-  const int d4 = tid & 7;
-  const int sl = tid >> 3;
-  float4v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = sl; s < nsb; s += kCombineThreads / 8) {
-    acc += s_w[s] * *(const float4v*)(rec(s) + g * kHeadDim + dc * kCombineDChunk + d4 * 4);
+  for (int s = sl + kCombinePerLane * kCombineSplitLanes; s < nsb; s += kCombineSplitLanes) {
+    mloc = fmaxf(mloc, rec(s)[mo + g]);
   }
-  s_acc[tid] = acc;
+
+  // Block max of the split maxima.
+  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+  if (lane == 0) s_red[tid >> 6] = mloc;
   __syncthreads();
-  for (int off = kCombineThreads / 16; off > 0; off >>= 1) {
-    if (sl < off) s_acc[tid] += s_acc[tid + off * 8];
+  float M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, s_red[w]);
+
+  float Ls = 0.f;
+  float4v o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kCombinePerLane; ++k) {
+    const int s = sl + k * kCombineSplitLanes;
+    if (s < nsb) {
+      const float w = exp2_fast(mv[k] - M);
+      Ls += w * lv[k];
+      o += w * ov[k];
+    }
+  }
+  for (int s = sl + kCombinePerLane * kCombineSplitLanes; s < nsb; s += kCombineSplitLanes) {
+    const float* r = rec(s);
+    const float w = exp2_fast(r[mo + g] - M);
+    Ls += w * r[mo + G + g];
+    o += w * *(const float4v*)(r + col);
+  }
+
+  // Sum over the 32 split lanes (fixed tree order).
+  s_acc[tid] = o;
+  s_ls[tid] = Ls;
+  __syncthreads();
+  for (int off = kCombineSplitLanes / 2; off > 0; off >>= 1) {
+    if (sl < off) {
+      s_acc[tid] += s_acc[tid + off * 8];
+      s_ls[tid] += s_ls[tid + off * 8];
+    }
     __syncthreads();
   }
   if (tid < 8) {
-    const float inv = 1.0f / L;
-    const float4v o = s_acc[tid];
+    const float inv = 1.0f / s_ls[tid];
+    const float4v r = s_acc[tid];
     uint2 packed;
-    packed.x = pack_half2(o[0] * inv, o[1] * inv);
-    packed.y = pack_half2(o[2] * inv, o[3] * inv);
+    packed.x = pack_half2(r[0] * inv, r[1] * inv);
+    packed.y = pack_half2(r[2] * inv, r[3] * inv);
     *(uint2*)(orow + tid * 4) = packed;
   }
 }
@@ -512,12 +564,12 @@ __global__ void widen_kernel(const uint8_t* in, uint16_t* out16, float* out32, l
 
 }  // namespace
 
-hipError_t launch_attend(const AttendArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(attend_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(split_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+hipError_t launch_combine(const AttendArgs& a, hipStream_t stream) {
   const int grid = a.batch * a.num_kv_heads * a.group * (kHeadDim / kCombineDChunk);
   hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
@@ -534,7 +586,7 @@ hipError_t launch_widen(const uint8_t* in, uint16_t* out_f16, float* out_f32, in
 }
 
 hipError_t attend_blocks_per_cu(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, attend_kernel, kThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, split_kernel, kThreads, 0);
 }
 
 }  // namespace xqa

@@ -67,7 +67,7 @@ typedef struct {
   int32_t page_size;         /* 16                                                      */
   int32_t max_pages_per_seq; /* >= 1: block-table row stride in int32 elements          */
   int32_t max_work_items;    /* 0: sized from the device's occupancy; else the split    */
-                             /* workgroup count (>= Hkv * (max_batch + 1))              */
+                             /* grid in workgroups, in [Hkv*(max_batch+1), Hkv*2048]    */
 } xqa_config_t;
 
 typedef struct {
@@ -81,9 +81,9 @@ typedef struct {
 } xqa_info_t;
 
 /* Create a handle on the current HIP device. Validates cfg, sizes the split
- * grid from the split kernel's occupancy and allocates the partial-result
- * workspace (the only allocation the library makes). *out_handle is set only
- * on XQA_OK. Errors: INVALID_ARG (null pointers, non-positive sizes),
+ * grid from the split kernel's occupancy and allocates the workspace for
+ * split states (the only allocation the library makes). *out_handle is set
+ * only on XQA_OK. Errors: INVALID_ARG (null pointers, non-positive sizes),
  * UNSUPPORTED (head_dim != 128, page_size != 16, Hq % Hkv != 0, G > 16),
  * OUT_OF_MEMORY, HIP (no device). */
 xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle);
@@ -101,24 +101,28 @@ xqa_status_t xqa_get_info(xqa_handle_t handle, xqa_info_t* info);
  * block_table and context_lens. batch must be in [1, max_batch]; scale must
  * be finite. q, k_pages, v_pages and out must be 16-byte aligned,
  * block_table and context_lens 4-byte aligned. The calling thread's current
- * device must be the handle's device. Errors: INVALID_ARG, HIP. */
+ * device must be the handle's device. Calls made with one handle must not
+ * overlap in time (they share the handle's workspace); calls on one stream
+ * never do. Errors: INVALID_ARG, HIP. */
 xqa_status_t xqa_decode(xqa_handle_t handle, const void* q, const uint8_t* k_pages,
                         const uint8_t* v_pages, const int32_t* block_table,
                         const int32_t* context_lens, int32_t batch, float scale,
                         void* out, void* stream);
 
-/* First stage of xqa_decode: plan, gather, widen, QK, online softmax, PV.
- * Rows whose sequence fits one work item are written to out directly; the
- * others leave per-item partial states in the workspace for
- * xqa_decode_combine, which must follow on the same stream with the same
- * context_lens, batch and out before the handle is used again. */
-xqa_status_t xqa_decode_attend(xqa_handle_t handle, const void* q, const uint8_t* k_pages,
-                               const uint8_t* v_pages, const int32_t* block_table,
-                               const int32_t* context_lens, int32_t batch, float scale,
-                               void* out, void* stream);
+/* First stage of xqa_decode alone (device-side plan, page gather, widening,
+ * QK, online softmax, PV): rows of sequences that fit one work item are
+ * written to out; the others leave split states in the workspace. Same
+ * arguments and errors as xqa_decode. xqa_decode_combine must follow on the
+ * same stream, with the same context_lens, batch and out, before the handle
+ * is used again. Exposed so the two stages can be timed or scheduled apart. */
+xqa_status_t xqa_decode_split(xqa_handle_t handle, const void* q, const uint8_t* k_pages,
+                              const uint8_t* v_pages, const int32_t* block_table,
+                              const int32_t* context_lens, int32_t batch, float scale,
+                              void* out, void* stream);
 
-/* Second stage: log-sum-exp merge of the partial states of every row that
- * was split, in a fixed order, plus zero rows for n <= 0. */
+/* Second stage of xqa_decode alone: log-sum-exp merge of the split states of
+ * every long sequence (fixed order) and zero rows for sequences with n <= 0.
+ * Errors: INVALID_ARG (null or misaligned pointers, batch out of range), HIP. */
 xqa_status_t xqa_decode_combine(xqa_handle_t handle, const int32_t* context_lens,
                                 int32_t batch, void* out, void* stream);
 

@@ -69,7 +69,7 @@ def test_null_arguments_are_rejected(lib):
     null = ctypes.c_void_p()
     args = [null] * 6 + [1, ctypes.c_float(0.1), null, null]
     assert lib.xqa_decode(*args) == 1
-    assert lib.xqa_decode_attend(*args) == 1
+    assert lib.xqa_decode_split(*args) == 1
     assert lib.xqa_decode_combine(null, null, 1, null, null) == 1
     assert lib.xqa_get_info(null, None) == 1
     assert lib.xqa_destroy(null) == 0

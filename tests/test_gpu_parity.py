@@ -148,16 +148,16 @@ def test_scale_zero_gives_mean_of_v():
 
 # -------------------------------------------------------------- invariants
 
-def test_repeat_stage_split_and_permutation_bitwise():
+def test_repeat_stages_and_permutation_bitwise():
     w = make_custom([3000, 17, 700, 4096, 1], 4, 32, 47, pool_pages=800)
     out, xqa, dev = run(w)
     for _ in range(20):
         again, _, _ = run(w, xqa=xqa, dev=dev)
         assert (again.view(np.uint32) == out.view(np.uint32)).all()
-    # attend + combine called separately == decode
+    # split + combine called separately == decode
     o2 = torch.empty_like(dev.q)
-    xqa.attend(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages, block_table=dev.block_table,
-               context_lens=dev.context_lens, scale=w.scale, out=o2)
+    xqa.split(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages, block_table=dev.block_table,
+              context_lens=dev.context_lens, scale=w.scale, out=o2)
     xqa.combine(context_lens=dev.context_lens, out=o2)
     torch.cuda.synchronize()
     assert (o2.float().cpu().numpy() == out).all()
