@@ -119,16 +119,14 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
     return fail(XQA_ERR_UNSUPPORTED, "num_q_heads must be a multiple of num_kv_heads");
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
   if (G > xqa::kMaxGroup) return fail(XQA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
-  if ((long long)cfg->max_pages_per_seq * xqa::kPageSize > (1LL << 30))
-    return fail(XQA_ERR_UNSUPPORTED, "max_pages_per_seq too large");
-  if (cfg->max_batch >= xqa::kMaxItemsPerHead)
-    return fail(XQA_ERR_UNSUPPORTED, "max_batch must be below 2048");
-  const long long min_grid = (long long)cfg->num_kv_heads * (cfg->max_batch + 1);
+  if (cfg->max_batch > xqa::kMaxBatch) return fail(XQA_ERR_UNSUPPORTED, "max_batch above 65536");
+  if ((long long)cfg->max_pages_per_seq * xqa::kPageSize > xqa::kMaxSeqTokens)
+    return fail(XQA_ERR_UNSUPPORTED, "max_pages_per_seq * page_size must not exceed 2^24 tokens");
+  const long long min_grid = cfg->num_kv_heads;
   const long long max_grid = (long long)cfg->num_kv_heads * xqa::kMaxItemsPerHead;
   if (cfg->max_work_items > 0 &&
       (cfg->max_work_items < min_grid || cfg->max_work_items > max_grid))
-    return fail(XQA_ERR_INVALID_ARG,
-                "max_work_items must lie in [Hkv*(max_batch+1), Hkv*2048]");
+    return fail(XQA_ERR_INVALID_ARG, "max_work_items must lie in [Hkv, Hkv*2048]");
 
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
@@ -143,7 +141,8 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
 
   long long grid = cfg->max_work_items;
   if (grid == 0) {
-    // Every item resident at once: one round of equal-sized items.
+    // Every item resident at once: one round of equal-sized items, the same
+    // number on every CU.
     grid = (long long)cus * per_cu;
     if (grid < min_grid) grid = min_grid;
     if (grid > max_grid) grid = max_grid;
@@ -151,7 +150,8 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
   const int per_head = (int)(grid / cfg->num_kv_heads);
   grid = (long long)per_head * cfg->num_kv_heads;
   const int stride = ((G * (xqa::kHeadDim + 2)) + 3) / 4 * 4;
-  const size_t ws = (size_t)grid * stride * sizeof(float);
+  // Two record slots per work item: its first and its last segment.
+  const size_t ws = (size_t)2 * grid * stride * sizeof(float);
 
   xqa_handle_s* h = new (std::nothrow) xqa_handle_s();
   if (!h) return fail(XQA_ERR_OUT_OF_MEMORY, "host allocation failed");
@@ -187,7 +187,7 @@ xqa_status_t xqa_get_info(xqa_handle_t h, xqa_info_t* info) {
   info->device = h->device;
   info->max_work_items = h->grid;
   info->items_per_head = h->per_head;
-  info->token_granule = xqa::kGranule;
+  info->token_granule = xqa::kBlockTokens;
   info->threads_per_item = xqa::kThreads;
   info->item_stride_floats = h->item_stride;
   info->workspace_bytes = (int64_t)h->workspace_bytes;
@@ -251,18 +251,11 @@ xqa_status_t xqa_plan(xqa_handle_t h, const int32_t* ctx, int32_t batch, int32_t
   if (batch < 1 || batch > h->cfg.max_batch)
     return fail(XQA_ERR_INVALID_ARG, "batch outside [1, max_batch]");
   const int max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
-  long long n_tot = 0;
-  int active = 0;
-  for (int b = 0; b < batch; ++b) {
-    const int n = xqa::clamp_len(ctx[b], max_tokens);
-    n_tot += n;
-    active += n > 0;
-  }
-  const int S = xqa::split_tokens(n_tot, active, h->per_head);
-  long long items = 0;
-  for (int b = 0; b < batch; ++b) items += xqa::num_splits(xqa::clamp_len(ctx[b], max_tokens), S);
-  *split_tokens = S;
-  *num_items = (int32_t)(items * h->cfg.num_kv_heads);
+  long long nb_total = 0;
+  for (int b = 0; b < batch; ++b) nb_total += xqa::seq_blocks(xqa::clamp_len(ctx[b], max_tokens));
+  const int P = xqa::items_per_head(nb_total, h->per_head);
+  *split_tokens = P > 0 ? (int32_t)((nb_total + P - 1) / P * xqa::kBlockTokens) : 0;
+  *num_items = P * h->cfg.num_kv_heads;
   return XQA_OK;
 }
 

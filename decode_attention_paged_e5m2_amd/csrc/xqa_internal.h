@@ -13,43 +13,55 @@ constexpr int kMaxGroup = 16;                          // query heads per KV hea
 constexpr int kWaves = 4;                              // waves per split workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlockTokens = 32;                       // tokens per wave iteration (2 pages)
-constexpr int kGranule = kWaves * kBlockTokens;        // split lengths are multiples of this
-constexpr int kMaxItemsPerHead = 2048;                 // bound on splits per sequence
+constexpr int kMinItemBlocks = 8;                      // smallest work item: 8 blocks = 256 tokens
+constexpr int kMaxItemsPerHead = 2048;                 // bound on work items per KV head
+constexpr int kMaxSeqTokens = 1 << 24;                 // bound on max_pages_per_seq * page_size
+constexpr int kMaxBatch = 1 << 16;                     // bound on max_batch
 constexpr int kCombineThreads = 256;
 constexpr int kCombineDChunk = 32;                     // head-dim columns per combine workgroup
 constexpr int kCombineSplitLanes = 32;                 // split lanes per combine workgroup
 constexpr int kCombinePerLane = 4;                     // split states a lane keeps in registers
 
 // ---------------------------------------------------------------------------
-// The split plan. Every workgroup of both kernels evaluates it on the device
-// from context_lens alone, so the grid never depends on
-// device data and a captured graph replays exactly with new lengths.
+// The balanced plan. Every workgroup of both kernels evaluates it on the
+// device from context_lens alone, so the grid never depends on device data
+// and a captured graph replays exactly with new lengths. Each KV head has the
+// same token structure; per head:
 //
-//   n_b    = clamp(context_lens[b], 0, max_tokens)
-//   N      = sum_b n_b,  A = #{b : n_b > 0}
-//   S      = granule * ceil(ceil(N / max(1, per_head - A)) / granule), S >= granule
-//   ns_b   = ceil(n_b / S) splits for sequence b
-//   items  = Hkv * sum_b ns_b  <=  Hkv * per_head  <=  grid
-// (sum_b ceil(n_b / S) <= N / S + A <= per_head because S >= N / (per_head - A)).
-// Work item i: h = i % Hkv, j = i / Hkv; the sequence b with
-// prefix_b <= j < prefix_b + ns_b, split s = j - prefix_b, tokens
-// [s*S, min(n_b, (s+1)*S)).
+//   n_b   = clamp(context_lens[b], 0, max_tokens)
+//   nb_b  = ceil(n_b / 32)              32-token blocks of sequence b
+//   off_b = sum_{b' < b} nb_b'          first block of b in the head's block stream
+//   NB    = sum_b nb_b
+//   P     = min(per_head, ceil(NB / 8))  work items (each at least 8 blocks)
+//   item i covers blocks [lo_i, lo_{i+1}) with lo_i = floor(i * NB / P), so
+//   every item holds floor(NB / P) or ceil(NB / P) blocks and every CU gets
+//   the same amount of KV bytes. Block x lies in item ceil((x + 1) P / NB) - 1.
+//
+// An item may span several sequences (segments). A sequence lying inside
+// one item is finished there; a longer one leaves one split state per item
+// it touches, in record slot 2i if it is item i's first segment and 2i + 1
+// if it is item i's last (and not first) segment.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int32_t clamp_len(int32_t n, int32_t max_tokens) {
   return n <= 0 ? 0 : (n > max_tokens ? max_tokens : n);
 }
 
-__host__ __device__ inline int32_t split_tokens(int64_t n_tot, int32_t active, int32_t per_head) {
-  int64_t denom = (int64_t)per_head - active;
-  if (denom < 1) denom = 1;
-  int64_t s = (n_tot + denom - 1) / denom;
-  s = (s + kGranule - 1) / kGranule * kGranule;
-  if (s < kGranule) s = kGranule;
-  return (int32_t)s;
+__host__ __device__ inline int32_t seq_blocks(int32_t n) {
+  return (n + kBlockTokens - 1) / kBlockTokens;
 }
 
-__host__ __device__ inline int32_t num_splits(int32_t n, int32_t S) {
-  return n <= 0 ? 0 : (n + S - 1) / S;
+__host__ __device__ inline int32_t items_per_head(int64_t nb_total, int32_t per_head) {
+  if (nb_total <= 0) return 0;
+  const int64_t p = (nb_total + kMinItemBlocks - 1) / kMinItemBlocks;
+  return p < per_head ? (int32_t)p : per_head;
+}
+
+__host__ __device__ inline int64_t item_lo(int64_t i, int64_t nb_total, int64_t items) {
+  return i * nb_total / items;
+}
+
+__host__ __device__ inline int32_t item_of_block(int64_t x, int64_t nb_total, int64_t items) {
+  return (int32_t)(((x + 1) * items + nb_total - 1) / nb_total - 1);
 }
 
 struct AttendArgs {

@@ -97,27 +97,9 @@ __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
 }
 
 // ---------------------------------------------------------------- the plan
-struct Totals {
-  long long n_tot;
-  int active;
-};
-
-__device__ Totals plan_totals(const int32_t* ctx, int batch, int max_tokens, int lane) {
-  long long sum = 0;
-  int cnt = 0;
-  for (int base = 0; base < batch; base += 64) {
-    const int i = base + lane;
-    const int n = i < batch ? clamp_len(ctx[i], max_tokens) : 0;
-    sum += n;
-    cnt += n > 0;
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    sum += __shfl_xor(sum, off);
-    cnt += __shfl_xor(cnt, off);
-  }
-  return {sum, cnt};
-}
-
+// Wave-level evaluation of the balanced plan (see xqa_internal.h). Each lane
+// reads the length of one sequence per 64-sequence chunk; prefix sums use
+// lane shuffles, so every call costs one pass over context_lens.
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   for (int off = 1; off < 64; off <<= 1) {
     const int t = __shfl_up(v, off);
@@ -126,46 +108,66 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-// Work index j (item / Hkv) -> (sequence b, split s, splits of b).
-__device__ bool plan_locate(const int32_t* ctx, int batch, int max_tokens, int S, int j, int lane,
-                            int& b, int& s, int& nsb) {
-  int prefix = 0;
-  for (int base = 0; base < batch; base += 64) {
-    const int i = base + lane;
-    const int ns = i < batch ? num_splits(clamp_len(ctx[i], max_tokens), S) : 0;
-    const int incl = wave_inclusive_scan(ns, lane);
-    const int lo = prefix + incl - ns;
-    const unsigned long long hit = __ballot(j >= lo && j < prefix + incl);
-    if (hit) {
-      const int src = __ffsll((unsigned long long)hit) - 1;
-      b = base + src;
-      nsb = __shfl(ns, src);
-      s = j - __shfl(lo, src);
-      return true;
-    }
-    prefix += __shfl(incl, 63);
-  }
-  return false;
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ long long uniform64(long long v) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(v & 0xFFFFFFFFll));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
+  return ((long long)hi << 32) | (unsigned)lo;
 }
 
-// Sequence b -> (splits of b, work index of its first split).
-__device__ void plan_row(const int32_t* ctx, int batch, int max_tokens, int S, int b, int lane,
-                         int& nsb, int& first) {
-  int prefix = 0;
-  nsb = 0;
-  first = 0;
+// Total 32-token blocks per head: NB = sum_b ceil(n_b / 32).
+__device__ long long plan_total_blocks(const int32_t* ctx, int batch, int max_tokens, int lane) {
+  long long sum = 0;
   for (int base = 0; base < batch; base += 64) {
     const int i = base + lane;
-    const int ns = i < batch ? num_splits(clamp_len(ctx[i], max_tokens), S) : 0;
-    const int incl = wave_inclusive_scan(ns, lane);
+    sum += i < batch ? seq_blocks(clamp_len(ctx[i], max_tokens)) : 0;
+  }
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  return uniform64(sum);
+}
+
+struct SeqInfo {
+  int b;          // sequence index
+  int n;          // clamped length
+  long long off;  // first block in the head's block stream
+};
+
+// Sequence b's length and block offset.
+__device__ SeqInfo seq_at(const int32_t* ctx, int batch, int max_tokens, int b, int lane) {
+  long long prefix = 0;
+  for (int base = 0; base < batch; base += 64) {
+    const int i = base + lane;
+    const int n = i < batch ? clamp_len(ctx[i], max_tokens) : 0;
+    const int nb = seq_blocks(n);
+    const int incl = wave_inclusive_scan(nb, lane);
     if (b < base + 64) {
       const int src = b - base;
-      nsb = __shfl(ns, src);
-      first = prefix + __shfl(incl - ns, src);
-      return;
+      return {b, uniform(__shfl(n, src)), uniform64(prefix + __shfl(incl - nb, src))};
     }
     prefix += __shfl(incl, 63);
   }
+  return {b, 0, prefix};
+}
+
+// The non-empty sequence whose blocks contain block x (x < NB).
+__device__ SeqInfo seq_containing(const int32_t* ctx, int batch, int max_tokens, long long x,
+                                  int lane) {
+  long long prefix = 0;
+  for (int base = 0; base < batch; base += 64) {
+    const int i = base + lane;
+    const int n = i < batch ? clamp_len(ctx[i], max_tokens) : 0;
+    const int nb = seq_blocks(n);
+    const int incl = wave_inclusive_scan(nb, lane);
+    const long long lo = prefix + incl - nb;
+    const unsigned long long hit = __ballot(nb > 0 && x >= lo && x < prefix + incl);
+    if (hit) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      return {base + src, uniform(__shfl(n, src)), uniform64(prefix + __shfl(incl - nb, src))};
+    }
+    prefix += __shfl(incl, 63);
+  }
+  return {batch, 0, prefix};
 }
 
 // ------------------------------------------------------------ split kernel
@@ -193,12 +195,12 @@ __device__ __forceinline__ void load_block(RawBlock& r, const uint8_t* ka, const
   r.v[3] = *(const u32x4*)(vb + voff + 64);
 }
 
-template <bool kTail>
 __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4], WaveState& st,
                                               float scale_log2e, int tok0, int t_end, int lane,
                                               uint32_t sel1, uint32_t selh0, uint32_t selh1) {
   const int q = lane >> 4;
-  if (kTail) {
+  const bool tail = tok0 + kBlockTokens > t_end;   // wave-uniform
+  if (tail) {
     // V rows of tokens past the end are zeroed (their bytes may be NaN codes
     // and 0 * NaN would poison the sum). V lane token: 4q + (lane & 3).
     const int tv = tok0 + 4 * q + (lane & 3);
@@ -234,7 +236,7 @@ __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4],
     z[r4] = sa[r4] * scale_log2e;
     z[4 + r4] = sb[r4] * scale_log2e;
   }
-  if (kTail) {
+  if (tail) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int t = tok0 + 4 * q + r4;
@@ -284,33 +286,23 @@ __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4],
   }
 }
 
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+struct SplitShared {
+  float m[kWaves][kMaxGroup];
+  float l[kWaves][kMaxGroup];
+  float o[kWaves][kMaxGroup][kHeadDim + 4];
+};
 
-__global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
-  __shared__ float s_m[kWaves][kMaxGroup];
-  __shared__ float s_l[kWaves][kMaxGroup];
-  __shared__ float s_o[kWaves][kMaxGroup][kHeadDim + 4];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+// One segment: blocks [jb_lo, jb_hi) of sequence b (tokens 32 jb_lo ..
+// min(n, 32 jb_hi)) for KV head h. The four waves take interleaved blocks,
+// then merge in LDS. `direct`: the segment is the whole sequence, so the
+// normalised output is written; otherwise the state goes to `rec`.
+__device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh, int b, int h,
+                                            int n, int jb_lo, int jb_hi, bool direct, float* rec,
+                                            int lane, int wave) {
   const int G = a.group;
   const int Hkv = a.num_kv_heads;
-  const int item = blockIdx.x;
-
-  const Totals tt = plan_totals(a.context_lens, a.batch, a.max_tokens, lane);
-  const int S = uniform(split_tokens(tt.n_tot, tt.active, a.per_head));
-
-  const int h = item % Hkv;
-  int b, s, nsb;
-  if (!plan_locate(a.context_lens, a.batch, a.max_tokens, S, item / Hkv, lane, b, s, nsb)) {
-    return;   // beyond the planned items: the whole workgroup leaves
-  }
-  b = uniform(b);
-  s = uniform(s);
-  nsb = uniform(nsb);
-  const int n = uniform(clamp_len(a.context_lens[b], a.max_tokens));
-  const int t_begin = s * S;
-  const int t_end = min(n, t_begin + S);
+  const int t_begin = jb_lo * kBlockTokens;
+  const int t_end = min(n, jb_hi * kBlockTokens);
   const int g = lane & 15;
   const int q = lane >> 4;
 
@@ -344,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
   const size_t page_stride = (size_t)Hkv * kPageHeadBytes;
   const uint8_t* kbase = a.k_pages + (size_t)h * kPageHeadBytes;
   const uint8_t* vbase = a.v_pages + (size_t)h * kPageHeadBytes;
-  const int nblocks = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
+  const int nblocks = jb_hi - jb_lo;
   const int my_blocks = nblocks > wave ? (nblocks - wave + kWaves - 1) / kWaves : 0;
   const int first_page = t_begin >> 4;
   const int last_page = (t_end - 1) >> 4;
@@ -366,59 +358,61 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
     };
     auto tok0 = [&](int mm) { return t_begin + (wave + kWaves * (c0 + mm)) * kBlockTokens; };
 
+    // Two buffers in turn: while one block is processed the next is in
+    // flight. Every load in the steady-state loop is unconditional, so the
+    // compiler's waits name exactly the buffer about to be used.
     RawBlock A, B;
     issue(A, 0);
     int mm = 0;
     for (; mm + 2 < cnt; mm += 2) {
       issue(B, mm + 1);
-      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
+      process_block(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
       issue(A, mm + 2);
-      process_block<false>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
+      process_block(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
     }
     if (cnt - mm == 2) {
       issue(B, mm + 1);
-      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
-      process_block<true>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
+      process_block(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
+      process_block(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
     } else {
-      process_block<true>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
+      process_block(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
     }
   }
 
   // Publish the wave's state.
   if (g < G) {
     if (q == 0) {
-      s_m[wave][g] = st.m;
-      s_l[wave][g] = st.l[0];
+      sh.m[wave][g] = st.m;
+      sh.l[wave][g] = st.l[0];
     }
 #pragma unroll
     for (int L = 0; L < 2; ++L) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        *(float4v*)&s_o[wave][g][64 * L + 16 * q + 4 * k] = st.o[L * 4 + k];
+        *(float4v*)&sh.o[wave][g][64 * L + 16 * q + 4 * k] = st.o[L * 4 + k];
       }
     }
   }
   __syncthreads();
 
-  // Merge the four waves (fixed order): the item's (max, sum, O).
+  // Merge the four waves (fixed order): the segment's (max, sum, O).
   uint16_t* out_group = a.out + ((long long)b * Hkv * G + (long long)h * G) * kHeadDim;
-  float* rec = a.partials + (long long)item * a.item_stride;
   for (int e = threadIdx.x; e < G * 32; e += kThreads) {
     const int gg = e >> 5;
     const int d4 = (e & 31) * 4;
-    float M = s_m[0][gg];
+    float M = sh.m[0][gg];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][gg]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.m[w][gg]);
     float Ls = 0.f;
     float4v o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = s_m[w][gg];
+      const float mw = sh.m[w][gg];
       const float f = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
-      Ls += f * s_l[w][gg];
-      o += f * *(const float4v*)&s_o[w][gg][d4];
+      Ls += f * sh.l[w][gg];
+      o += f * *(const float4v*)&sh.o[w][gg][d4];
     }
-    if (nsb == 1) {
+    if (direct) {
       const float inv = 1.0f / Ls;
       uint2 packed;
       packed.x = pack_half2(o[0] * inv, o[1] * inv);
@@ -431,6 +425,39 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
         rec[G * kHeadDim + G + gg] = Ls;
       }
     }
+  }
+  __syncthreads();   // the LDS state is reused by the next segment
+}
+
+__global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
+  __shared__ SplitShared sh;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int Hkv = a.num_kv_heads;
+
+  const long long NB = plan_total_blocks(a.context_lens, a.batch, a.max_tokens, lane);
+  const int P = items_per_head(NB, a.per_head);
+  const int item = blockIdx.x / Hkv;
+  const int h = blockIdx.x % Hkv;
+  if (item >= P) return;   // the whole workgroup leaves
+  const long long lo = item_lo(item, NB, P);
+  const long long hi = item_lo(item + 1, NB, P);
+
+  SeqInfo sq = seq_containing(a.context_lens, a.batch, a.max_tokens, lo, lane);
+  bool first = true;
+  while (true) {
+    const int nb = seq_blocks(sq.n);
+    const long long seg_lo = lo > sq.off ? lo : sq.off;
+    const long long seg_hi = hi < sq.off + nb ? hi : sq.off + nb;
+    const bool direct = item_of_block(sq.off, NB, P) == item_of_block(sq.off + nb - 1, NB, P);
+    float* rec = a.partials + ((long long)(2 * item + (first ? 0 : 1)) * Hkv + h) * a.item_stride;
+    run_segment(a, sh, sq.b, h, sq.n, (int)(seg_lo - sq.off), (int)(seg_hi - sq.off), direct, rec,
+                lane, wave);
+    if (sq.off + nb >= hi) break;
+    first = false;
+    do {   // next non-empty sequence (one exists: this item has blocks left)
+      sq = seq_at(a.context_lens, a.batch, a.max_tokens, sq.b + 1, lane);
+    } while (sq.n == 0);
   }
 }
 
@@ -455,17 +482,21 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) 
   const int hq = (blk / kChunks) % Hq;
   const int b = blk / (kChunks * Hq);
 
-  const Totals tt = plan_totals(a.context_lens, a.batch, a.max_tokens, lane);
-  const int S = uniform(split_tokens(tt.n_tot, tt.active, a.per_head));
-  const int n = clamp_len(a.context_lens[b], a.max_tokens);
+  const long long NB = plan_total_blocks(a.context_lens, a.batch, a.max_tokens, lane);
+  const int P = items_per_head(NB, a.per_head);
+  const SeqInfo sq = seq_at(a.context_lens, a.batch, a.max_tokens, b, lane);
   uint16_t* orow = a.out + ((long long)b * Hq + hq) * kHeadDim + dc * kCombineDChunk;
-  if (n == 0) {
+  if (sq.n == 0) {
     if (tid < kCombineDChunk) orow[tid] = 0;
     return;
   }
-  int nsb, first;
-  plan_row(a.context_lens, a.batch, a.max_tokens, S, b, lane, nsb, first);
-  if (nsb <= 1) return;   // written by the split kernel
+  const int i0 = item_of_block(sq.off, NB, P);
+  const int i1 = item_of_block(sq.off + seq_blocks(sq.n) - 1, NB, P);
+  if (i0 == i1) return;   // written by the split kernel
+  const int nsb = i1 - i0 + 1;
+  // Item i0 holds this sequence in slot 2*i0 if the sequence starts its
+  // block range, else in slot 2*i0 + 1; later items hold it in slot 2*i.
+  const int slot0 = (sq.off == item_lo(i0, NB, P)) ? 2 * i0 : 2 * i0 + 1;
 
   const int h = hq / G;
   const int g = hq % G;
@@ -473,7 +504,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) 
   const int col = g * kHeadDim + dc * kCombineDChunk + (tid & 7) * 4;
   const int sl = tid >> 3;
   auto rec = [&](int s) {
-    return a.partials + ((long long)(first + s) * Hkv + h) * a.item_stride;
+    const int slot = s == 0 ? slot0 : 2 * (i0 + s);
+    return a.partials + ((long long)slot * Hkv + h) * a.item_stride;
   };
 
   float mv[kCombinePerLane], lv[kCombinePerLane];

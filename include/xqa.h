@@ -26,7 +26,8 @@
  *     block_table  int32    [batch][max_pages_per_seq], row stride max_pages_per_seq
  *     context_lens int32    [batch]
  *     out          binary16 [batch][Hq][head_dim], contiguous
- * Supported shapes: head_dim 128, page_size 16, 1 <= G <= 16.
+ * Supported shapes: head_dim 128, page_size 16, 1 <= G <= 16,
+ * max_pages_per_seq * page_size <= 2^24.
  *
  * Device-resident values are not validated (that would need a device->host
  * copy and would break graph capture). Contract: block-table entries that a
@@ -67,16 +68,16 @@ typedef struct {
   int32_t page_size;         /* 16                                                      */
   int32_t max_pages_per_seq; /* >= 1: block-table row stride in int32 elements          */
   int32_t max_work_items;    /* 0: sized from the device's occupancy; else the split    */
-                             /* grid in workgroups, in [Hkv*(max_batch+1), Hkv*2048]    */
+                             /* grid in workgroups, in [Hkv, Hkv*2048]                  */
 } xqa_config_t;
 
 typedef struct {
   int32_t device;            /* HIP device the handle was created on                    */
   int32_t max_work_items;    /* grid of the split kernel                                */
-  int32_t items_per_head;    /* max_work_items / Hkv: bound on splits per sequence      */
-  int32_t token_granule;     /* split lengths are multiples of this many tokens         */
+  int32_t items_per_head;    /* max_work_items / Hkv: work items per KV head (at most)  */
+  int32_t token_granule;     /* work items are whole blocks of this many tokens         */
   int32_t threads_per_item;  /* workgroup size of the split kernel                      */
-  int32_t item_stride_floats;/* floats per partial record in the workspace              */
+  int32_t item_stride_floats;/* floats per split-state record (two records per item)    */
   int64_t workspace_bytes;   /* device bytes the handle owns                            */
 } xqa_info_t;
 
@@ -84,7 +85,8 @@ typedef struct {
  * grid from the split kernel's occupancy and allocates the workspace for
  * split states (the only allocation the library makes). *out_handle is set
  * only on XQA_OK. Errors: INVALID_ARG (null pointers, non-positive sizes),
- * UNSUPPORTED (head_dim != 128, page_size != 16, Hq % Hkv != 0, G > 16),
+ * UNSUPPORTED (head_dim != 128, page_size != 16, Hq % Hkv != 0, G > 16,
+ * max_batch > 65536, more than 2^24 tokens per sequence),
  * OUT_OF_MEMORY, HIP (no device). */
 xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle);
 
@@ -127,8 +129,10 @@ xqa_status_t xqa_decode_combine(xqa_handle_t handle, const int32_t* context_lens
                                 int32_t batch, void* out, void* stream);
 
 /* Host mirror of the device-side plan, for diagnostics and tests:
- * context_lens_host is host memory [batch]. Writes the split length in
- * tokens and the number of split work items the device would use. */
+ * context_lens_host is host memory [batch]. Each KV head's token stream
+ * (sequences in batch order, each rounded up to 32-token blocks) is cut into
+ * equal block ranges, one per work item. Writes the largest work item in
+ * tokens and the number of work items (all heads) the device would use. */
 xqa_status_t xqa_plan(xqa_handle_t handle, const int32_t* context_lens_host, int32_t batch,
                       int32_t* split_tokens, int32_t* num_items);
 

@@ -53,7 +53,8 @@ def _cfg(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(head_dim=64), 2), (dict(page_size=32), 2), (dict(num_q_heads=30), 2),
     (dict(num_q_heads=68, num_kv_heads=4), 2), (dict(max_batch=0), 1),
-    (dict(max_pages_per_seq=0), 1), (dict(max_work_items=5), 1), (dict(max_batch=4096), 2),
+    (dict(max_pages_per_seq=0), 1), (dict(max_work_items=3), 1), (dict(max_work_items=9000), 1),
+    (dict(max_batch=70000), 2), (dict(max_pages_per_seq=(1 << 20) + 1), 2),
 ])
 def test_create_rejects_bad_configs_before_hip(lib, over, status):
     h = ctypes.c_void_p()

@@ -95,18 +95,30 @@ def test_context_sweep_1_to_64(hkv, hq):
     log(f"sweep hkv={hkv} hq={hq}", st)
 
 
-def test_split_boundaries():
-    # Lengths on both sides of the split length S the plan picks, and of the
-    # 32-token block and 128-token granule inside an item.
-    probe = Xqa(max_batch=12, num_q_heads=16, num_kv_heads=2, max_pages_per_seq=512)
-    base = [4000, 4000, 4000, 4000, 4000, 4000]
-    S, _ = probe.plan(base + [1] * 6)
-    ctx = base + [S - 1, S, S + 1, 2 * S + 31, 2 * S + 32, 2 * S + 33]
-    S2, items = probe.plan(ctx)
-    w = make_custom(ctx, 2, 16, 42, pool_pages=12 * 512, max_pages_per_seq=512)
-    out, _, _ = run(w, xqa=probe)
-    st = assert_parity(out, reference(w), f"split boundaries S={S2} items={items}")
-    log(f"boundaries S={S2} items={items}", st)
+def test_work_item_boundaries():
+    # Few work items per head force items that span several sequences and
+    # sequences that span several items; lengths sit on both sides of the
+    # item and 32-token block boundaries.
+    rng = np.random.default_rng(41)
+    for per_head in (1, 3, 7, 0):
+        ctx = [1, 31, 32, 33, 255, 256, 257, 700, 2048, 2049, 3000, 5]
+        ctx = ctx[:12]
+        probe = Xqa(max_batch=12, num_q_heads=16, num_kv_heads=2, max_pages_per_seq=256,
+                    max_work_items=2 * per_head)
+        S, items = probe.plan(ctx)
+        w = make_custom(ctx, 2, 16, [42, per_head], pool_pages=12 * 256, max_pages_per_seq=256)
+        out, _, _ = run(w, xqa=probe)
+        st = assert_parity(out, reference(w), f"per_head={per_head} S={S} items={items}")
+        log(f"item boundaries per_head={per_head} S={S} items={items}", st)
+    # sequences exactly one item long, then shifted by one block
+    for shift in (0, 32, 1):
+        ctx = [8 * 32] * 6
+        ctx[0] += shift
+        probe = Xqa(max_batch=6, num_q_heads=8, num_kv_heads=1, max_pages_per_seq=32,
+                    max_work_items=6)
+        w = make_custom(ctx, 1, 8, [43, shift], pool_pages=6 * 32, max_pages_per_seq=32)
+        out, _, _ = run(w, xqa=probe)
+        assert_parity(out, reference(w), f"aligned items shift={shift}")
 
 
 def test_zero_and_negative_lengths_and_clamp():
