@@ -12,7 +12,8 @@ replays and the rotating footprint exceeds the on-package caches.
 Order: generate -> upload -> CPU baseline leg (the float64 oracle timed on
 the host cores; its output is also the correctness gate for variant 0) ->
 graph gate (every variant's replay bitwise equal to its eager call) ->
-independent warm-up of each arm -> timed graph replays (the headline) ->
+independent warm-up of each arm -> timed replays of one graph holding R
+consecutive steps (the headline; one-step-per-graph replays are reported too) ->
 A/B/B/A eager vs graph blocks -> per-launch HIP-event timing of the split
 kernel (the dominant one) and of the combine kernel on the stream they are
 launched on. Prints one JSON line.
@@ -43,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=0, help="oracle repetitions (0 = auto, ~10-20 s)")
     ap.add_argument("--quick", action="store_true", help="skip A/B/B/A and warm-mode extras")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (5x), the reference "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counter readings")
     return ap.parse_args()
 
 
@@ -102,6 +106,17 @@ def main():
         return 1
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                          "dispatches": 5}))
+        return 0
 
     t0 = time.time()
     works = [make_config(args.config, v) for v in range(args.variants)]
@@ -168,9 +183,31 @@ def main():
 
     R = len(graphs)
 
+    # One graph holding R consecutive decode steps (one per input variant),
+    # as a model's decode step holds one attention call per layer: the
+    # graph-launch cost is paid once per R steps instead of once per step.
+    multi = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(multi):
+        for d, o in zip(devs, outs):
+            call(d, o)
+    torch.cuda.synchronize()
+    for o in outs:
+        o.fill_(float("nan"))
+    multi.replay()
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        if not torch.equal(o.view(torch.int16), eager[i].view(torch.int16)):
+            print(json.dumps({"error": f"multi-step graph differs from eager (variant {i})"}))
+            return 1
+    log(f"{R}-step graph == eager bitwise")
+
     def run_graph(n_steps, start=0):
         for s in range(n_steps):
             graphs[(start + s) % R].replay()
+
+    def run_multi(n_steps):
+        for _ in range(n_steps // R):
+            multi.replay()
 
     def run_eager(n_steps, start=0):
         for s in range(n_steps):
@@ -178,21 +215,34 @@ def main():
             call(devs[i], outs[i])
 
     # ---------------------------------------------------- headline timing
+    # Steps are replays of the R-step graph; K is rounded up to a multiple
+    # of R so every variant is stepped equally often.
+    steps = -(-args.steps // R) * R
     run_eager(args.warmup)                 # each arm warms up on its own
     torch.cuda.synchronize()
     run_graph(args.warmup)
     torch.cuda.synchronize()
+    run_multi(max(args.warmup, R))
+    torch.cuda.synchronize()
     t_start = time.perf_counter()
-    run_graph(args.steps)
+    run_multi(steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    steps_bytes = sum(kv_bytes[s % R] for s in range(args.steps))
+    steps_bytes = sum(kv_bytes[s % R] for s in range(steps))
     gbs = steps_bytes / elapsed / 1e9
-    us_step = elapsed / args.steps * 1e6
-    log(f"graph replay: {us_step:.2f} us/step, {gbs:.1f} GB/s KV ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+    us_step = elapsed / steps * 1e6
+    log(f"{R}-step graph replay: {us_step:.2f} us/step, {gbs:.1f} GB/s KV "
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
 
-    detail = {"us_per_step_graph": us_step, "kv_bytes_per_step_mean": statistics.mean(kv_bytes),
-              "handle": info}
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    run_graph(steps)
+    torch.cuda.synchronize()
+    us_1 = (time.perf_counter() - t1) / steps * 1e6
+    log(f"1-step graph replay: {us_1:.2f} us/step")
+
+    detail = {"us_per_step_graph_Rstep": us_step, "us_per_step_graph_1step": us_1,
+              "kv_bytes_per_step_mean": statistics.mean(kv_bytes), "handle": info}
 
     # ------------------------------------------------------ A/B/B/A blocks
     if not args.quick:
@@ -245,7 +295,7 @@ def main():
         "value": gbs,
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": us_step / 1e3,
         "higher_is_better": True,
@@ -258,7 +308,8 @@ def main():
             "batch": w0.batch, "num_kv_heads": w0.num_kv_heads, "num_q_heads": w0.num_q_heads,
             "head_dim": w0.head_dim, "page_size": w0.page_size, "kv_dtype": "fp8_e5m2",
             "context_lens": "variant-dependent; " + ",".join(str(w.total_tokens) for w in works) + " tokens",
-            "variants": R, "timed_as": "hipGraph replay, variants cycled",
+            "variants": R,
+            "timed_as": f"hipGraph replay, one graph of {R} consecutive decode steps (one per input variant)",
             "pct_of_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
             "us_per_step": us_step,
         },

@@ -166,7 +166,7 @@ def test_repeat_stages_and_permutation_bitwise():
     for _ in range(20):
         again, _, _ = run(w, xqa=xqa, dev=dev)
         assert (again.view(np.uint32) == out.view(np.uint32)).all()
-    # split + combine called separately == decode
+    # split + combine called separately == decode, bitwise
     o2 = torch.empty_like(dev.q)
     xqa.split(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages, block_table=dev.block_table,
               context_lens=dev.context_lens, scale=w.scale, out=o2)
@@ -182,6 +182,25 @@ def test_repeat_stages_and_permutation_bitwise():
     bt2 = perm[dev.block_table.long()].to(torch.int32)
     o3, _, _ = run(w, xqa=xqa, dev=dev, k_pages=k2, v_pages=v2, block_table=bt2)
     assert (o3 == out).all()
+
+
+def test_alternating_inputs_never_read_stale_split_states():
+    # The workspace holds split states from call to call; reading one left by
+    # the previous call (different inputs) would change the bits. Alternate
+    # two inputs and require every output to equal that input's first output.
+    ws = [make_custom([5000, 3000, 77, 9000], 2, 16, [50, v], pool_pages=1400,
+                      max_pages_per_seq=600) for v in range(2)]
+    devs = [to_device(w) for w in ws]
+    xqa = Xqa(max_batch=4, num_q_heads=16, num_kv_heads=2, max_pages_per_seq=600)
+    firsts = []
+    for w, d in zip(ws, devs):
+        o, _, _ = run(w, xqa=xqa, dev=d)
+        assert_parity(o, reference(w), "alternating first")
+        firsts.append(o)
+    for rep in range(100):
+        i = rep % 2
+        o, _, _ = run(ws[i], xqa=xqa, dev=devs[i])
+        assert (o.view(np.uint32) == firsts[i].view(np.uint32)).all(), f"repeat {rep}"
 
 
 def test_output_canaries_untouched():
