@@ -33,6 +33,34 @@ if ROOT not in sys.path:
 METRIC = "us per decode step + achieved KV-read HBM GB/s (% of peak), B16 ragged ~17.8K"
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes per split-kernel launch on the ragged B16 workload, from
+# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes (KiB per dispatch, mean over
+# the variants), scaled by what the same counters read for a plain 1 GiB copy
+# (FETCH_SIZE x2.00, WRITE_SIZE x1.00). Valid only for the kernel sources
+# whose hash is recorded; any change to them reports null until re-measured.
+MEASURED_TRAFFIC = {
+    "sources_sha256": "b3b1a5fe4fb4a6719a608aeb9c356c5187cc855da890ca7cbeb36c4d1fdad8af",
+    "fetch_kib": 133370.7, "fetch_scale": 2.0,
+    "write_kib": 2323.8, "write_scale": 1.0,
+}
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_paged_e5m2_amd", "csrc")
+    for f in ("xqa_kernels.hip", "xqa_internal.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic_bytes(config):
+    t = MEASURED_TRAFFIC
+    if config != 4 or kernel_sources_sha256() != t["sources_sha256"]:
+        return None
+    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -314,7 +342,7 @@ def main():
             "us_per_step": us_step,
         },
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic_bytes(args.config)},
         "cpu_baseline": cpu,
         "detail": detail,
     }
