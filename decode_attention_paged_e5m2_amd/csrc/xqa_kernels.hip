@@ -45,7 +45,8 @@
 //
 // The combine kernel then merges the states of every split sequence with
 // the exact log-sum-exp rule M = max m_s, L = sum l_s 2^(m_s-M),
-// out = sum 2^(m_s-M) O_s / L, and writes the zero rows of empty sequences.
+// out = sum 2^(m_s-M) O_s / L (split order, in rounds of kCombineRound
+// states), and writes the zero rows of empty sequences.
 // The kernel boundary makes the split states visible across the chip's
 // separately cached dies without any in-kernel cache write-back.
 //
@@ -462,114 +463,82 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
 }
 
 // ----------------------------------------------------------- combine kernel
-// One workgroup per (sequence, query head, 32-column chunk); thread t is
-// split lane t/8 (splits t/8, t/8 + 32, ...) and column lane t%8 (4 columns).
-// Every state a thread needs is loaded in one round, so the kernel costs two
-// dependent memory round trips (lengths, then states) plus LDS reductions.
+// One workgroup per (sequence, KV head). Thread t owns output columns
+// 4(t%32) .. 4(t%32)+3 of query head t/32 of the group and reads exactly that
+// slice of every split state, kCombineRound states per round with all loads
+// issued before any is used: one memory round trip per round (one for most
+// sequences), no cross-thread reduction, and few waves to dispatch.
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) {
-  __shared__ float s_red[kCombineThreads / 64];
-  __shared__ float4v s_acc[kCombineThreads];
-  __shared__ float s_ls[kCombineThreads];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane = threadIdx.x & 63;
   const int G = a.group;
   const int Hkv = a.num_kv_heads;
-  const int Hq = Hkv * G;
-  constexpr int kChunks = kHeadDim / kCombineDChunk;
-  const int blk = blockIdx.x;
-  const int dc = blk % kChunks;
-  const int hq = (blk / kChunks) % Hq;
-  const int b = blk / (kChunks * Hq);
+  const int b = blockIdx.x / Hkv;
+  const int h = blockIdx.x % Hkv;
 
   const long long NB = plan_total_blocks(a.context_lens, a.batch, a.max_tokens, lane);
   const int P = items_per_head(NB, a.per_head);
   const SeqInfo sq = seq_at(a.context_lens, a.batch, a.max_tokens, b, lane);
-  uint16_t* orow = a.out + ((long long)b * Hq + hq) * kHeadDim + dc * kCombineDChunk;
+  uint16_t* out_group = a.out + ((long long)b * Hkv * G + (long long)h * G) * kHeadDim;
   if (sq.n == 0) {
-    if (tid < kCombineDChunk) orow[tid] = 0;
+    uint4* z = (uint4*)out_group;
+    for (int e = threadIdx.x; e < G * kHeadDim / 8; e += kCombineThreads) z[e] = uint4{0, 0, 0, 0};
     return;
   }
   const int i0 = item_of_block(sq.off, NB, P);
-  const int i1 = item_of_block(sq.off + seq_blocks(sq.n) - 1, NB, P);
-  if (i0 == i1) return;   // written by the split kernel
-  const int nsb = i1 - i0 + 1;
+  const int nsb = item_of_block(sq.off + seq_blocks(sq.n) - 1, NB, P) - i0 + 1;
+  if (nsb == 1) return;   // written by the split kernel
   // Item i0 holds this sequence in slot 2*i0 if the sequence starts its
   // block range, else in slot 2*i0 + 1; later items hold it in slot 2*i.
   const int slot0 = (sq.off == item_lo(i0, NB, P)) ? 2 * i0 : 2 * i0 + 1;
-
-  const int h = hq / G;
-  const int g = hq % G;
   const int mo = G * kHeadDim;
-  const int col = g * kHeadDim + dc * kCombineDChunk + (tid & 7) * 4;
-  const int sl = tid >> 3;
   auto rec = [&](int s) {
     const int slot = s == 0 ? slot0 : 2 * (i0 + s);
     return a.partials + ((long long)slot * Hkv + h) * a.item_stride;
   };
 
-  float mv[kCombinePerLane], lv[kCombinePerLane];
-  float4v ov[kCombinePerLane];
-  float mloc = -INFINITY;
+  for (int e0 = 0; e0 < G * 32; e0 += kCombineThreads) {
+    const int e = e0 + threadIdx.x;
+    if (e >= G * 32) break;
+    const int gg = e >> 5;
+    const int col = gg * kHeadDim + (e & 31) * 4;
+    float M = -INFINITY, Ls = 0.f;
+    float4v o = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsb; s0 += kCombineRound) {
+      const int cnt = min(kCombineRound, nsb - s0);
+      float mv[kCombineRound], lv[kCombineRound];
+      float4v ov[kCombineRound];
 #pragma unroll
-  for (int k = 0; k < kCombinePerLane; ++k) {
-    const int s = sl + k * kCombineSplitLanes;
-    if (s < nsb) {
-      const float* r = rec(s);
-      mv[k] = r[mo + g];
-      lv[k] = r[mo + G + g];
-      ov[k] = *(const float4v*)(r + col);
-      mloc = fmaxf(mloc, mv[k]);
-    }
-  }
-  for (int s = sl + kCombinePerLane * kCombineSplitLanes; s < nsb; s += kCombineSplitLanes) {
-    mloc = fmaxf(mloc, rec(s)[mo + g]);
-  }
-
-  // Block max of the split maxima.
-  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-  if (lane == 0) s_red[tid >> 6] = mloc;
-  __syncthreads();
-  float M = s_red[0];
+      for (int k = 0; k < kCombineRound; ++k) {
+        if (k < cnt) {
+          const float* r = rec(s0 + k);
+          ov[k] = *(const float4v*)(r + col);
+          mv[k] = r[mo + gg];
+          lv[k] = r[mo + G + gg];
+        }
+      }
+      float mr = M;
 #pragma unroll
-  for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, s_red[w]);
-
-  float Ls = 0.f;
-  float4v o = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < kCombineRound; ++k) {
+        if (k < cnt) mr = fmaxf(mr, mv[k]);
+      }
+      const float fa = exp2_fast(M - mr);   // rescales earlier rounds (0 on the first)
+      Ls *= fa;
+      o *= fa;
+      M = mr;
 #pragma unroll
-  for (int k = 0; k < kCombinePerLane; ++k) {
-    const int s = sl + k * kCombineSplitLanes;
-    if (s < nsb) {
-      const float w = exp2_fast(mv[k] - M);
-      Ls += w * lv[k];
-      o += w * ov[k];
+      for (int k = 0; k < kCombineRound; ++k) {
+        if (k < cnt) {
+          const float w = exp2_fast(mv[k] - M);
+          Ls += w * lv[k];
+          o += w * ov[k];
+        }
+      }
     }
-  }
-  for (int s = sl + kCombinePerLane * kCombineSplitLanes; s < nsb; s += kCombineSplitLanes) {
-    const float* r = rec(s);
-    const float w = exp2_fast(r[mo + g] - M);
-    Ls += w * r[mo + G + g];
-    o += w * *(const float4v*)(r + col);
-  }
-
-  // Sum over the 32 split lanes (fixed tree order).
-  s_acc[tid] = o;
-  s_ls[tid] = Ls;
-  __syncthreads();
-  for (int off = kCombineSplitLanes / 2; off > 0; off >>= 1) {
-    if (sl < off) {
-      s_acc[tid] += s_acc[tid + off * 8];
-      s_ls[tid] += s_ls[tid + off * 8];
-    }
-    __syncthreads();
-  }
-  if (tid < 8) {
-    const float inv = 1.0f / s_ls[tid];
-    const float4v r = s_acc[tid];
+    const float inv = 1.0f / Ls;
     uint2 packed;
-    packed.x = pack_half2(r[0] * inv, r[1] * inv);
-    packed.y = pack_half2(r[2] * inv, r[3] * inv);
-    *(uint2*)(orow + tid * 4) = packed;
+    packed.x = pack_half2(o[0] * inv, o[1] * inv);
+    packed.y = pack_half2(o[2] * inv, o[3] * inv);
+    *(uint2*)(out_group + col) = packed;
   }
 }
 
@@ -602,7 +571,7 @@ hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const AttendArgs& a, hipStream_t stream) {
-  const int grid = a.batch * a.num_kv_heads * a.group * (kHeadDim / kCombineDChunk);
+  const int grid = a.batch * a.num_kv_heads;
   hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
