@@ -17,7 +17,8 @@ constexpr int kMinItemBlocks = 8;                      // smallest work item: 8 
 constexpr int kMaxItemsPerHead = 2048;                 // bound on work items per KV head
 constexpr int kMaxSeqTokens = 1 << 24;                 // bound on max_pages_per_seq * page_size
 constexpr int kMaxBatch = 1 << 16;                     // bound on max_batch
-constexpr int kCombineThreads = 256;                   // one combine workgroup per (sequence, KV head)
+constexpr int kCombineThreads = 64;                    // one wave per combine workgroup
+constexpr int kCombineChunks = 8;                      // combine workgroups per (sequence, KV head)
 constexpr int kCombineRound = 16;                      // split states loaded per round
 
 // ---------------------------------------------------------------------------

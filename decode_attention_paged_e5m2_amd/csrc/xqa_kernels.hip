@@ -463,25 +463,30 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
 }
 
 // ----------------------------------------------------------- combine kernel
-// One workgroup per (sequence, KV head). Thread t owns output columns
-// 4(t%32) .. 4(t%32)+3 of query head t/32 of the group and reads exactly that
-// slice of every split state, kCombineRound states per round with all loads
-// issued before any is used: one memory round trip per round (one for most
-// sequences), no cross-thread reduction, and few waves to dispatch.
+// One single-wave workgroup per (sequence, KV head, 16-column chunk): a long
+// sequence's many split states are read by kCombineChunks CUs at once. Lane
+// t owns columns 2(t%8), 2(t%8)+1 of the chunk for query head t/8 and reads
+// exactly that slice of every split state, kCombineRound states per round
+// with all loads issued before any is used: one memory round trip per round
+// (one for most sequences) and no cross-lane reduction.
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) {
   const int lane = threadIdx.x & 63;
   const int G = a.group;
   const int Hkv = a.num_kv_heads;
-  const int b = blockIdx.x / Hkv;
-  const int h = blockIdx.x % Hkv;
+  const int chunk = blockIdx.x % kCombineChunks;
+  const int bh = blockIdx.x / kCombineChunks;
+  const int b = bh / Hkv;
+  const int h = bh % Hkv;
+  constexpr int kCols = kHeadDim / kCombineChunks;   // 16 columns per chunk
 
   const long long NB = plan_total_blocks(a.context_lens, a.batch, a.max_tokens, lane);
   const int P = items_per_head(NB, a.per_head);
   const SeqInfo sq = seq_at(a.context_lens, a.batch, a.max_tokens, b, lane);
   uint16_t* out_group = a.out + ((long long)b * Hkv * G + (long long)h * G) * kHeadDim;
   if (sq.n == 0) {
-    uint4* z = (uint4*)out_group;
-    for (int e = threadIdx.x; e < G * kHeadDim / 8; e += kCombineThreads) z[e] = uint4{0, 0, 0, 0};
+    for (int e = threadIdx.x; e < G * kCols / 2; e += kCombineThreads) {
+      *(uint32_t*)(out_group + (e / (kCols / 2)) * kHeadDim + chunk * kCols + (e % (kCols / 2)) * 2) = 0;
+    }
     return;
   }
   const int i0 = item_of_block(sq.off, NB, P);
@@ -496,49 +501,42 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) 
     return a.partials + ((long long)slot * Hkv + h) * a.item_stride;
   };
 
-  for (int e0 = 0; e0 < G * 32; e0 += kCombineThreads) {
-    const int e = e0 + threadIdx.x;
-    if (e >= G * 32) break;
-    const int gg = e >> 5;
-    const int col = gg * kHeadDim + (e & 31) * 4;
+  for (int e = threadIdx.x; e < G * kCols / 2; e += kCombineThreads) {
+    const int gg = e / (kCols / 2);
+    const int col = gg * kHeadDim + chunk * kCols + (e % (kCols / 2)) * 2;
     float M = -INFINITY, Ls = 0.f;
-    float4v o = {0.f, 0.f, 0.f, 0.f};
+    float o0 = 0.f, o1 = 0.f;
     for (int s0 = 0; s0 < nsb; s0 += kCombineRound) {
       const int cnt = min(kCombineRound, nsb - s0);
       float mv[kCombineRound], lv[kCombineRound];
-      float4v ov[kCombineRound];
+      float2 ov[kCombineRound];
+      // Unconditional loads (slots past the last split re-read it and are
+      // masked below), so the whole round is in flight at once.
 #pragma unroll
       for (int k = 0; k < kCombineRound; ++k) {
-        if (k < cnt) {
-          const float* r = rec(s0 + k);
-          ov[k] = *(const float4v*)(r + col);
-          mv[k] = r[mo + gg];
-          lv[k] = r[mo + G + gg];
-        }
+        const float* r = rec(min(s0 + k, nsb - 1));
+        ov[k] = *(const float2*)(r + col);
+        mv[k] = r[mo + gg];
+        lv[k] = r[mo + G + gg];
       }
       float mr = M;
 #pragma unroll
-      for (int k = 0; k < kCombineRound; ++k) {
-        if (k < cnt) mr = fmaxf(mr, mv[k]);
-      }
+      for (int k = 0; k < kCombineRound; ++k) mr = fmaxf(mr, k < cnt ? mv[k] : -INFINITY);
       const float fa = exp2_fast(M - mr);   // rescales earlier rounds (0 on the first)
       Ls *= fa;
-      o *= fa;
+      o0 *= fa;
+      o1 *= fa;
       M = mr;
 #pragma unroll
       for (int k = 0; k < kCombineRound; ++k) {
-        if (k < cnt) {
-          const float w = exp2_fast(mv[k] - M);
-          Ls += w * lv[k];
-          o += w * ov[k];
-        }
+        const float w = k < cnt ? exp2_fast(mv[k] - M) : 0.f;
+        Ls += w * lv[k];
+        o0 += w * ov[k].x;
+        o1 += w * ov[k].y;
       }
     }
     const float inv = 1.0f / Ls;
-    uint2 packed;
-    packed.x = pack_half2(o[0] * inv, o[1] * inv);
-    packed.y = pack_half2(o[2] * inv, o[3] * inv);
-    *(uint2*)(out_group + col) = packed;
+    *(uint32_t*)(out_group + col) = pack_half2(o0 * inv, o1 * inv);
   }
 }
 
@@ -571,7 +569,7 @@ hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const AttendArgs& a, hipStream_t stream) {
-  const int grid = a.batch * a.num_kv_heads;
+  const int grid = a.batch * a.num_kv_heads * kCombineChunks;
   hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
