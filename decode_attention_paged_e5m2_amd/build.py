@@ -14,10 +14,12 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "xqa_kernels.hip"), os.path.join(CSRC, "xqa_api.cpp")]
 ARCH = "gfx950"
 
-# Packed-FP32 instructions are disabled for all device code.
+# Packed-FP32 instructions are disabled for all device code. MFMA results
+# are kept in ordinary VGPRs (no AGPR copies around the softmax arithmetic).
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE,
 ]
 

@@ -92,6 +92,22 @@ __device__ __forceinline__ void transpose_widen(uint32_t x, uint32_t sel1, uint3
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum of v over lane pairs (l, l ^ 16) and (l, l ^ 32). With both
+// operands equal, a permlane swap returns, in its two results, the lane's own
+// value and its partner's (in either order), so their maximum is the pair's.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Headroom of the reference maximum (base-2 units): weights are at most
+// 2^8 = 256, far inside binary16 and fp32 range.
+constexpr float kRescaleSlack = 8.0f;
+
 __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
   half2v h = {(_Float16)a, (_Float16)b};
   return __builtin_bit_cast(uint32_t, h);
@@ -196,11 +212,14 @@ __device__ __forceinline__ void load_block(RawBlock& r, const uint8_t* ka, const
   r.v[3] = *(const u32x4*)(vb + voff + 64);
 }
 
+// kTail: the block may extend past t_end (only a wave's last block of a
+// segment can); other blocks skip the masking.
+template <bool kTail>
 __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4], WaveState& st,
                                               float scale_log2e, int tok0, int t_end, int lane,
                                               uint32_t sel1, uint32_t selh0, uint32_t selh1) {
   const int q = lane >> 4;
-  const bool tail = tok0 + kBlockTokens > t_end;   // wave-uniform
+  const bool tail = kTail && tok0 + kBlockTokens > t_end;   // wave-uniform
   if (tail) {
     // V rows of tokens past the end are zeroed (their bytes may be NaN codes
     // and 0 * NaN would poison the sum). V lane token: 4q + (lane & 3).
@@ -230,38 +249,62 @@ __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4],
     sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, fb), qf[i], sb, 0, 0, 0);
   }
 
-  // Scale (base 2), mask, online softmax.
-  float z[8];
+  // Scores in base-2 units are c * s (c = scale * log2 e). A full block
+  // takes the extreme raw score and folds c into the exponent's fma; the
+  // tail block scales first so that masked tokens are exactly -inf.
+  float s8[8];
 #pragma unroll
   for (int r4 = 0; r4 < 4; ++r4) {
-    z[r4] = sa[r4] * scale_log2e;
-    z[4 + r4] = sb[r4] * scale_log2e;
+    s8[r4] = sa[r4];
+    s8[4 + r4] = sb[r4];
   }
+  float bm;
   if (tail) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int t = tok0 + 4 * q + r4;
-      if (t >= t_end) z[r4] = -INFINITY;
-      if (t + kPageSize >= t_end) z[4 + r4] = -INFINITY;
+      s8[r4] = t >= t_end ? -INFINITY : s8[r4] * scale_log2e;
+      s8[4 + r4] = t + kPageSize >= t_end ? -INFINITY : s8[4 + r4] * scale_log2e;
     }
+    bm = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])),
+               fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
+  } else {
+    // max_i(c s_i) = c max_i s_i for c >= 0 and c min_i s_i otherwise,
+    // exactly: rounding is monotonic.
+    const float hi = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])),
+                           fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
+    const float lo = fminf(fminf(fminf(s8[0], s8[1]), fminf(s8[2], s8[3])),
+                           fminf(fminf(s8[4], s8[5]), fminf(s8[6], s8[7])));
+    bm = (scale_log2e >= 0.f ? hi : lo) * scale_log2e;
   }
-  float bm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                   fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
-  const float m_new = fmaxf(st.m, bm);
-  const float alpha = exp2_fast(st.m - m_new);
-  st.m = m_new;
-
-  u32x4 pf;
-#pragma unroll
-  for (int r2 = 0; r2 < 4; ++r2) {
-    pf[r2] = pack_half2(exp2_fast(z[2 * r2] - m_new), exp2_fast(z[2 * r2 + 1] - m_new));
-  }
-  if (__any(alpha != 1.0f)) {
+  bm = max_xor16(bm);   // the four lane quarters of a head agree on the maximum
+  bm = max_xor32(bm);
+  // st.m is a reference maximum, not the running one: it is raised only when
+  // a score exceeds it by more than kRescaleSlack (base-2 units), so weights
+  // stay below 2^kRescaleSlack and the state is rescaled on few blocks. Any
+  // reference gives the same softmax; the merges below use it as such.
+  if (__any(bm > st.m + kRescaleSlack)) {
+    const float m_new = fmaxf(st.m, bm);
+    const float alpha = exp2_fast(st.m - m_new);
+    st.m = m_new;
 #pragma unroll
     for (int t = 0; t < 8; ++t) st.o[t] *= alpha;
     st.l *= alpha;
+  }
+  const float m_ref = st.m;
+
+  u32x4 pf;
+  if (tail) {
+#pragma unroll
+    for (int r2 = 0; r2 < 4; ++r2) {
+      pf[r2] = pack_half2(exp2_fast(s8[2 * r2] - m_ref), exp2_fast(s8[2 * r2 + 1] - m_ref));
+    }
+  } else {
+#pragma unroll
+    for (int r2 = 0; r2 < 4; ++r2) {
+      pf[r2] = pack_half2(exp2_fast(fmaf(s8[2 * r2], scale_log2e, -m_ref)),
+                          exp2_fast(fmaf(s8[2 * r2 + 1], scale_log2e, -m_ref)));
+    }
   }
 
   // PV: V^T tiles from the quad transpose, P^T straight from the scores.
@@ -367,16 +410,16 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
     int mm = 0;
     for (; mm + 2 < cnt; mm += 2) {
       issue(B, mm + 1);
-      process_block(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
+      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
       issue(A, mm + 2);
-      process_block(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
+      process_block<false>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
     }
     if (cnt - mm == 2) {
       issue(B, mm + 1);
-      process_block(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
-      process_block(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
+      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
+      process_block<true>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
     } else {
-      process_block(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
+      process_block<true>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
     }
   }
 
