@@ -187,6 +187,47 @@ __device__ SeqInfo seq_containing(const int32_t* ctx, int batch, int max_tokens,
   return {batch, 0, prefix};
 }
 
+// The lookups the kernels make, with one pass over context_lens. For
+// batch <= 64 the pass leaves sequence `lane`'s length and block prefix in
+// lane registers, and every later lookup is a v_readlane or a ballot with no
+// memory access; larger batches rescan context_lens per lookup.
+struct SeqTable {
+  const int32_t* ctx;
+  int batch, max_tokens;
+  bool small;      // batch <= 64
+  int n_l;         // small: clamped length of sequence `lane` (0 past the batch)
+  int excl_l;      // small: first block of sequence `lane`
+  long long nb;    // total blocks per head
+
+  __device__ SeqTable(const int32_t* c, int bt, int mt, int lane)
+      : ctx(c), batch(bt), max_tokens(mt), small(bt <= 64), n_l(0), excl_l(0), nb(0) {
+    if (small) {
+      n_l = lane < batch ? clamp_len(ctx[lane], max_tokens) : 0;
+      const int b_l = seq_blocks(n_l);
+      const int incl = wave_inclusive_scan(b_l, lane);   // <= 64 * 2^19: no overflow
+      excl_l = incl - b_l;
+      nb = uniform(__shfl(incl, 63));
+    } else {
+      nb = plan_total_blocks(ctx, batch, max_tokens, lane);
+    }
+  }
+
+  __device__ SeqInfo at(int b, int lane) const {
+    if (!small) return seq_at(ctx, batch, max_tokens, b, lane);
+    if (b >= 64) return {b, 0, nb};
+    return {b, __builtin_amdgcn_readlane(n_l, b), (long long)__builtin_amdgcn_readlane(excl_l, b)};
+  }
+
+  __device__ SeqInfo containing(long long x, int lane) const {
+    if (!small) return seq_containing(ctx, batch, max_tokens, x, lane);
+    const unsigned long long hit =
+        __ballot(n_l > 0 && x >= excl_l && x < excl_l + seq_blocks(n_l));
+    if (!hit) return {batch, 0, nb};
+    const int src = __ffsll((unsigned long long)hit) - 1;
+    return {src, __builtin_amdgcn_readlane(n_l, src), (long long)__builtin_amdgcn_readlane(excl_l, src)};
+  }
+};
+
 // ------------------------------------------------------------ split kernel
 struct RawBlock {
   u32x4 k[4];   // page a: loads 0, 1; page b: loads 2, 3
@@ -479,7 +520,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
   const int wave = threadIdx.x >> 6;
   const int Hkv = a.num_kv_heads;
 
-  const long long NB = plan_total_blocks(a.context_lens, a.batch, a.max_tokens, lane);
+  const SeqTable seqs(a.context_lens, a.batch, a.max_tokens, lane);
+  const long long NB = seqs.nb;
   const int P = items_per_head(NB, a.per_head);
   const int item = blockIdx.x / Hkv;
   const int h = blockIdx.x % Hkv;
@@ -487,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
   const long long lo = item_lo(item, NB, P);
   const long long hi = item_lo(item + 1, NB, P);
 
-  SeqInfo sq = seq_containing(a.context_lens, a.batch, a.max_tokens, lo, lane);
+  SeqInfo sq = seqs.containing(lo, lane);
   bool first = true;
   while (true) {
     const int nb = seq_blocks(sq.n);
@@ -500,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
     if (sq.off + nb >= hi) break;
     first = false;
     do {   // next non-empty sequence (one exists: this item has blocks left)
-      sq = seq_at(a.context_lens, a.batch, a.max_tokens, sq.b + 1, lane);
+      sq = seqs.at(sq.b + 1, lane);
     } while (sq.n == 0);
   }
 }
@@ -522,9 +564,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) 
   const int h = bh % Hkv;
   constexpr int kCols = kHeadDim / kCombineChunks;   // 16 columns per chunk
 
-  const long long NB = plan_total_blocks(a.context_lens, a.batch, a.max_tokens, lane);
+  const SeqTable seqs(a.context_lens, a.batch, a.max_tokens, lane);
+  const long long NB = seqs.nb;
   const int P = items_per_head(NB, a.per_head);
-  const SeqInfo sq = seq_at(a.context_lens, a.batch, a.max_tokens, b, lane);
+  const SeqInfo sq = seqs.at(b, lane);
   uint16_t* out_group = a.out + ((long long)b * Hkv * G + (long long)h * G) * kHeadDim;
   if (sq.n == 0) {
     for (int e = threadIdx.x; e < G * kCols / 2; e += kCombineThreads) {

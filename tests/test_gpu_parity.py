@@ -121,6 +121,27 @@ def test_work_item_boundaries():
         assert_parity(out, reference(w), f"aligned items shift={shift}")
 
 
+@pytest.mark.parametrize("batch,per_head", [(65, 0), (129, 5), (700, 0), (700, 3)])
+def test_large_batches(batch, per_head):
+    # More than 64 sequences: the plan scans context_lens 64 sequences at a
+    # time. Ragged lengths with empty sequences (one right at the 64-sequence
+    # boundary) and a few long ones; a small per_head makes work items cross
+    # sequence and 64-sequence boundaries.
+    rng = np.random.default_rng(1000 + batch + per_head)
+    ctx = rng.integers(1, 300, size=batch)
+    ctx[rng.random(batch) < 0.15] = 0
+    ctx[63] = 0
+    ctx[[3, 64, batch - 1]] = [2100, 1500, 777]
+    w = make_custom(ctx.tolist(), 2, 16, [51, batch, per_head])
+    xqa = Xqa(max_batch=batch, num_q_heads=16, num_kv_heads=2,
+              max_pages_per_seq=w.max_pages_per_seq, max_work_items=2 * per_head)
+    out, _, _ = run(w, xqa=xqa)
+    S, items = xqa.plan(w.context_lens)
+    st = assert_parity(out, reference(w), f"batch={batch} per_head={per_head}")
+    assert (out[ctx == 0] == 0).all()
+    log(f"large batch={batch} per_head={per_head} S={S} items={items}", st)
+
+
 def test_zero_and_negative_lengths_and_clamp():
     # Sequence 3 fills its three pages; a length beyond the block table's
     # capacity clamps to 3 * 16 = 48 tokens.
