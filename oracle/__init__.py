@@ -30,6 +30,10 @@ All arithmetic is float64 numpy. Functions:
 * ``attention.partial_state`` / ``attention.merge_states``  the split-context
   form (running max, sum of weights, unnormalised output) and its
   log-sum-exp merge, used to pin the split-K + combine arithmetic.
+* ``append.encode_e5m2``        float -> E5M2 code, nearest finite value with
+  ties to even (the KV append's rounding)
+* ``append.append_kv``          the KV append: each sequence's new token
+  encoded and written to its page slot
 
 Pins (tests marked ``not gpu``): all 256 codes against the IEEE binary16 view
 of the code shifted into the high byte; single-token, constant-V, uniform-K,
@@ -38,6 +42,7 @@ pure-Python brute force on tiny shapes; split-and-merge equals single pass.
 """
 
 from .e5m2 import decode_e5m2, E5M2_TABLE, E5M2_MAX_FINITE
+from .append import encode_e5m2, append_kv
 from .attention import (
     decode_attention,
     decode_attention_row,
@@ -55,4 +60,6 @@ __all__ = [
     "gather_tokens",
     "partial_state",
     "merge_states",
+    "encode_e5m2",
+    "append_kv",
 ]
