@@ -146,6 +146,38 @@ class Xqa:
                                                   _stream_ptr(stream, self.device)))
         return out
 
+    def append_kv(self, *, k_new: torch.Tensor, v_new: torch.Tensor, block_table: torch.Tensor,
+                  context_lens: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                  batch: Optional[int] = None, stream: Optional[torch.cuda.Stream] = None) -> None:
+        """Write each sequence's new token (k_new, v_new: float16 [B, Hkv, 128]) into the
+        pages as E5M2 (xqa_append_kv); context_lens counts the new token."""
+        dev = self.device
+        if batch is None:
+            batch = k_new.shape[0] if isinstance(k_new, torch.Tensor) else 0
+        for name, t, dt in (("k_new", k_new, torch.float16), ("v_new", v_new, torch.float16),
+                            ("block_table", block_table, torch.int32),
+                            ("context_lens", context_lens, torch.int32),
+                            ("k_pages", k_pages, torch.uint8), ("v_pages", v_pages, torch.uint8)):
+            _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+            _need(t.dtype == dt, f"{name} must be {dt}")
+            _need(t.device == dev, f"{name} must be on {dev}")
+            _need(t.is_contiguous(), f"{name} must be contiguous")
+        H, D, P = self.num_kv_heads, self.head_dim, self.page_size
+        _need(1 <= batch <= self.max_batch, "batch outside [1, max_batch]")
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            _need(t.dim() == 3 and t.shape[0] >= batch and t.shape[1:] == (H, D),
+                  f"{name} must be [>= batch, {H}, {D}]")
+        for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+            _need(t.dim() == 4 and t.shape[1:] == (H, P, D), f"{name} must be [pages, {H}, {P}, {D}]")
+        _need(block_table.dim() == 2 and block_table.shape[0] >= batch
+              and block_table.shape[1] == self.max_pages_per_seq,
+              "block_table must be [>= batch, max_pages_per_seq]")
+        _need(context_lens.dim() == 1 and context_lens.shape[0] >= batch,
+              "context_lens must be [>= batch]")
+        _lib.check(_lib.load().xqa_append_kv(self._h, _ptr(k_new), _ptr(v_new), _ptr(block_table),
+                                             _ptr(context_lens), int(batch), _ptr(k_pages),
+                                             _ptr(v_pages), _stream_ptr(stream, dev)))
+
     # ----------------------------------------------------------- lifetime
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value is not None:

@@ -244,6 +244,36 @@ xqa_status_t xqa_decode(xqa_handle_t h, const void* q, const uint8_t* k_pages,
   return XQA_OK;
 }
 
+xqa_status_t xqa_append_kv(xqa_handle_t h, const void* k_new, const void* v_new,
+                           const int32_t* block_table, const int32_t* context_lens, int32_t batch,
+                           uint8_t* k_pages, uint8_t* v_pages, void* stream) {
+  if (!h) return fail(XQA_ERR_INVALID_ARG, "null handle");
+  if (!k_new || !v_new || !block_table || !context_lens || !k_pages || !v_pages)
+    return fail(XQA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16))
+    return fail(XQA_ERR_INVALID_ARG, "k_new, v_new, k_pages and v_pages must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4))
+    return fail(XQA_ERR_INVALID_ARG, "block_table and context_lens must be 4-byte aligned");
+  if (batch < 1 || batch > h->cfg.max_batch)
+    return fail(XQA_ERR_INVALID_ARG, "batch outside [1, max_batch]");
+  xqa_status_t st = check_device(h);
+  if (st != XQA_OK) return st;
+  xqa::AppendArgs a;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.batch = batch;
+  a.num_kv_heads = h->cfg.num_kv_heads;
+  a.max_pages = h->cfg.max_pages_per_seq;
+  a.max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
+  hipError_t e = xqa::launch_append(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+  return XQA_OK;
+}
+
 xqa_status_t xqa_plan(xqa_handle_t h, const int32_t* ctx, int32_t batch, int32_t* split_tokens,
                       int32_t* num_items) {
   if (!h || !ctx || !split_tokens || !num_items)

@@ -81,8 +81,24 @@ struct AttendArgs {
   float scale_log2e;      // scale * log2(e): scores are kept in base-2 units
 };
 
+// KV append: each sequence's new token (binary16 K and V rows for every KV
+// head) encoded to E5M2 and written to its page slot.
+struct AppendArgs {
+  const uint16_t* k_new;         // [batch][Hkv][128] binary16
+  const uint16_t* v_new;         // [batch][Hkv][128] binary16
+  const int32_t* block_table;
+  const int32_t* context_lens;   // lengths after the append
+  uint8_t* k_pages;
+  uint8_t* v_pages;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t max_pages;
+  int32_t max_tokens;
+};
+
 hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream);
 hipError_t launch_combine(const AttendArgs& a, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_widen(const uint8_t* in, uint16_t* out_f16, float* out_f32, int64_t n,
                         hipStream_t stream);
 hipError_t attend_blocks_per_cu(int* blocks);

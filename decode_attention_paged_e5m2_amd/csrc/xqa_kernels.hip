@@ -626,6 +626,52 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) 
   }
 }
 
+// ---------------------------------------------------------------- KV append
+// E5M2 code of a binary16 value. E5M2 is the high byte of binary16 (same
+// sign, exponent field and bias), so rounding the 16-bit pattern to its high
+// byte, to nearest even, is exact rounding of the value; subnormals and the
+// carry into the exponent need no special case. Past the largest finite code
+// 0x7B (57344) the nearest finite value is 0x7B: saturation, infinities
+// included. NaN gives 0x7F. The sign is kept.
+__device__ __forceinline__ uint32_t e5m2_from_f16(uint32_t h) {
+  const uint32_t sign = (h >> 8) & 0x80u;
+  const uint32_t mag = h & 0x7FFFu;
+  uint32_t r = (mag + 0x7Fu + ((mag >> 8) & 1u)) >> 8;
+  r = r > 0x7Bu ? 0x7Bu : r;
+  r = mag > 0x7C00u ? 0x7Fu : r;
+  return sign | r;
+}
+
+// One thread per (sequence, KV head, K or V, 8 head-dim values): a 16-byte
+// read of the new row, an 8-byte write into the page slot. 16 consecutive
+// threads cover one 128-value row, so reads and writes are contiguous.
+__global__ void append_kernel(AppendArgs a) {
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)a.batch * a.num_kv_heads * 32;
+  if (gid >= total) return;
+  const int j = (int)(gid & 15);
+  const int is_v = (int)((gid >> 4) & 1);
+  const long long bh = gid >> 5;   // b * Hkv + h
+  const int h = (int)(bh % a.num_kv_heads);
+  const int b = (int)(bh / a.num_kv_heads);
+  const int n = a.context_lens[b];
+  if (n <= 0 || n > a.max_tokens) return;   // no slot for this sequence
+  const int t = n - 1;
+  const int page = a.block_table[(long long)b * a.max_pages + t / kPageSize];
+  const uint16_t* src = (is_v ? a.v_new : a.k_new) + bh * kHeadDim + 8 * j;
+  const u32x4 x = *(const u32x4*)src;
+  uint32_t packed[2];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t p0 = x[2 * w], p1 = x[2 * w + 1];
+    packed[w] = e5m2_from_f16(p0 & 0xFFFFu) | (e5m2_from_f16(p0 >> 16) << 8) |
+                (e5m2_from_f16(p1 & 0xFFFFu) << 16) | (e5m2_from_f16(p1 >> 16) << 24);
+  }
+  uint8_t* dst = (is_v ? a.v_pages : a.k_pages) +
+                 (((size_t)page * a.num_kv_heads + h) * kPageSize + t % kPageSize) * kHeadDim + 8 * j;
+  *(uint2*)dst = make_uint2(packed[0], packed[1]);
+}
+
 // ------------------------------------------------------------ widen (test)
 // Each thread widens one group of four codes with the same helpers the K
 // path uses, so every byte position of both selectors is exercised.
@@ -657,6 +703,14 @@ hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream) {
 hipError_t launch_combine(const AttendArgs& a, hipStream_t stream) {
   const int grid = a.batch * a.num_kv_heads * kCombineChunks;
   hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kCombineThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  const long long total = (long long)a.batch * a.num_kv_heads * 32;
+  const int threads = 256;
+  const long long blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -128,6 +128,30 @@ xqa_status_t xqa_decode_split(xqa_handle_t handle, const void* q, const uint8_t*
 xqa_status_t xqa_decode_combine(xqa_handle_t handle, const int32_t* context_lens,
                                 int32_t batch, void* out, void* stream);
 
+/* KV append: write each sequence's new token into the paged cache, the step
+ * that precedes decode (page "[Kernel][SM70] Pipeline batched E5M2 XQA
+ * decode", section Purpose: the deployment keeps K and V as FP8 E5M2).
+ *     n = context_lens[b]           length after the append; the new token is n - 1
+ *     page = block_table[b][(n - 1) / page_size], slot = (n - 1) % page_size
+ *     k_pages[page][h][slot][:] = E5M2(k_new[b][h][:]) for every KV head h; same for V
+ * E5M2() rounds each binary16 value to the nearest finite E5M2 value, ties to
+ * even: values past 57344 and infinities give +-57344, the sign is kept (a
+ * negative value that rounds to zero gives -0), NaN gives 0x7F with its sign.
+ * Sequences with n <= 0 or n > max_pages_per_seq * page_size are not written.
+ * Layout (device memory, owned by the caller):
+ *     k_new, v_new  binary16 [batch][Hkv][head_dim], contiguous, 16-byte aligned
+ *     block_table, context_lens  as for xqa_decode
+ *     k_pages, v_pages  as for xqa_decode (written), 16-byte aligned
+ * The page receiving a token must not be the target of another sequence in
+ * the same call. Only the 2 * Hkv * head_dim bytes of each target slot are
+ * written. The call allocates nothing and never waits on the host, so it can
+ * be captured together with xqa_decode, which must come after it on the same
+ * stream. Errors: INVALID_ARG (null or misaligned pointers, batch outside
+ * [1, max_batch]), HIP. */
+xqa_status_t xqa_append_kv(xqa_handle_t handle, const void* k_new, const void* v_new,
+                           const int32_t* block_table, const int32_t* context_lens, int32_t batch,
+                           uint8_t* k_pages, uint8_t* v_pages, void* stream);
+
 /* Host mirror of the device-side plan, for diagnostics and tests:
  * context_lens_host is host memory [batch]. Each KV head's token stream
  * (sequences in batch order, each rounded up to 32-token blocks) is cut into

@@ -72,6 +72,7 @@ def test_null_arguments_are_rejected(lib):
     assert lib.xqa_decode(*args) == 1
     assert lib.xqa_decode_split(*args) == 1
     assert lib.xqa_decode_combine(null, null, 1, null, null) == 1
+    assert lib.xqa_append_kv(null, null, null, null, null, 1, null, null, null) == 1
     assert lib.xqa_get_info(null, None) == 1
     assert lib.xqa_destroy(null) == 0
     assert lib.xqa_debug_widen_e5m2(null, null, null, 4, null) == 1
