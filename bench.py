@@ -16,7 +16,8 @@ independent warm-up of each arm -> timed replays of one graph holding R
 consecutive steps (the headline; one-step-per-graph replays are reported too) ->
 A/B/B/A eager vs graph blocks -> per-launch HIP-event timing of the split
 kernel (the dominant one) and of the combine kernel on the stream they are
-launched on. Prints one JSON line.
+launched on -> the KV append (xqa_append_kv) per launch and in a graph of
+append + decode steps, reported in detail. Prints one JSON line.
 """
 
 import argparse
@@ -317,6 +318,53 @@ def main():
     detail["combine_kernel_us_mean"] = statistics.mean(comb_ms) * 1e3
     log(f"split kernel: {split_avg_us:.2f} us mean per launch -> {achieved:.1f} GB/s "
         f"({100 * achieved / HBM_PEAK_GBS:.1f}% of peak); combine {detail['combine_kernel_us_mean']:.2f} us")
+
+    # ------------------------------------------------------------ KV append
+    # The step before decode in serving: each sequence's new token written
+    # into its page slot as E5M2 (xqa_append_kv). Timed per launch with HIP
+    # events on the launch stream, and inside one graph holding append +
+    # decode for each of the R steps. It rewrites token n - 1 of every
+    # sequence, so it runs after every decode measurement above.
+    gen = torch.Generator().manual_seed(7)
+    k_new = [torch.randn((w.batch, w.num_kv_heads, w.head_dim), generator=gen).half().to(dev)
+             for w in works]
+    v_new = [torch.randn((w.batch, w.num_kv_heads, w.head_dim), generator=gen).half().to(dev)
+             for w in works]
+
+    def append(i):
+        d = devs[i]
+        xqa.append_kv(k_new=k_new[i], v_new=v_new[i], block_table=d.block_table,
+                      context_lens=d.context_lens, k_pages=d.k_pages, v_pages=d.v_pages)
+
+    for i in range(R):
+        append(i)
+    torch.cuda.synchronize()
+    ev_a = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(n_ev)]
+    for k in range(n_ev):
+        ev_a[k][0].record(stream)
+        append(k % R)
+        ev_a[k][1].record(stream)
+    torch.cuda.synchronize()
+    append_us = statistics.mean(ev_a[k][0].elapsed_time(ev_a[k][1]) for k in range(n_ev)) * 1e3
+    full = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(full):
+        for i in range(R):
+            append(i)
+            call(devs[i], outs[i])
+    for _ in range(max(args.warmup // R, 2)):
+        full.replay()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps // R):
+        full.replay()
+    torch.cuda.synchronize()
+    us_full = (time.perf_counter() - t) / steps * 1e6
+    detail["append_kv"] = {
+        "us_per_launch_mean": append_us,
+        "bytes_per_launch": w0.batch * w0.num_kv_heads * w0.head_dim * 2 * (2 + 1),
+        "us_per_step_graph_Rstep_append_plus_decode": us_full,
+    }
+    log(f"KV append: {append_us:.2f} us per launch; append + decode graph {us_full:.2f} us/step")
 
     line = {
         "metric": METRIC,
