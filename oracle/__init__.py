@@ -27,6 +27,8 @@ All arithmetic is float64 numpy. Functions:
 * ``e5m2.decode_e5m2``          closed-form E5M2 code -> float64
 * ``attention.decode_attention``  the full batched operation (float64 output)
 * ``attention.decode_attention_row``  one (sequence, query head) row
+* ``attention.decode_attention_multi``  M new query tokens per sequence,
+  causal among themselves
 * ``attention.partial_state`` / ``attention.merge_states``  the split-context
   form (running max, sum of weights, unnormalised output) and its
   log-sum-exp merge, used to pin the split-K + combine arithmetic.
@@ -45,6 +47,7 @@ from .e5m2 import decode_e5m2, E5M2_TABLE, E5M2_MAX_FINITE
 from .append import encode_e5m2, append_kv
 from .attention import (
     decode_attention,
+    decode_attention_multi,
     decode_attention_row,
     gather_tokens,
     partial_state,
@@ -57,6 +60,7 @@ __all__ = [
     "E5M2_MAX_FINITE",
     "decode_attention",
     "decode_attention_row",
+    "decode_attention_multi",
     "gather_tokens",
     "partial_state",
     "merge_states",

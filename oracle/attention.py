@@ -134,3 +134,37 @@ def merge_states(states):
         L += l * f
         acc = acc + f * np.asarray(o, dtype=np.float64)
     return acc / L
+
+
+def decode_attention_multi(q, k_pages, v_pages, block_table, context_lens, scale) -> np.ndarray:
+    """Several new query tokens per sequence, causal among themselves: float64 [B, M, Hq, D].
+
+    q is [B, M, Hq, D]. Reading taken (the pages name multi-token rows but do
+    not define them): n = min(context_lens[b], capacity) counts the M new
+    tokens, so query token j sits at position n - M + j and sees tokens
+    0 .. n - M + j, each through the same paged gather as a single query.
+    A query that sees no token (n - M + j < 0) gives a zero row.
+    """
+    q = np.asarray(q)
+    B, M, Hq, D = q.shape
+    Hkv = k_pages.shape[1]
+    P = k_pages.shape[2]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    s64 = _as_f64_scale(scale)
+    out = np.zeros((B, M, Hq, D), dtype=np.float64)
+    for b in range(B):
+        n = _effective_len(context_lens, block_table, P, b)
+        for j in range(M):
+            visible = n - M + j + 1
+            if visible <= 0:
+                continue
+            for h in range(Hkv):
+                K = gather_tokens(k_pages, block_table, b, h, visible)
+                V = gather_tokens(v_pages, block_table, b, h, visible)
+                Qg = np.asarray(q[b, j, h * G:(h + 1) * G, :], dtype=np.float64)   # [G, D]
+                Z = s64 * (Qg @ K.T)
+                W = np.exp(Z - Z.max(axis=1, keepdims=True))
+                out[b, j, h * G:(h + 1) * G, :] = (W @ V) / W.sum(axis=1, keepdims=True)
+    return out
