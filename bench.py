@@ -16,8 +16,9 @@ independent warm-up of each arm -> timed replays of one graph holding R
 consecutive steps (the headline; one-step-per-graph replays are reported too) ->
 A/B/B/A eager vs graph blocks -> per-launch HIP-event timing of the split
 kernel (the dominant one) and of the combine kernel on the stream they are
-launched on -> the KV append (xqa_append_kv) per launch and in a graph of
-append + decode steps, reported in detail. Prints one JSON line.
+launched on -> two query tokens per sequence (xqa_decode_multi) and the KV
+append (xqa_append_kv) per launch and in a graph of append + decode steps,
+reported in detail. Prints one JSON line.
 """
 
 import argparse
@@ -318,6 +319,44 @@ def main():
     detail["combine_kernel_us_mean"] = statistics.mean(comb_ms) * 1e3
     log(f"split kernel: {split_avg_us:.2f} us mean per launch -> {achieved:.1f} GB/s "
         f"({100 * achieved / HBM_PEAK_GBS:.1f}% of peak); combine {detail['combine_kernel_us_mean']:.2f} us")
+
+    # ------------------------------------------------- multi-token decode
+    # Two new query tokens per sequence (causal between them): the G query
+    # heads of a KV head times two tokens fill the 16-row matrix-core tile
+    # that one token leaves half empty at G = 8; the KV bytes are the same.
+    G = w0.num_q_heads // w0.num_kv_heads
+    if 2 * G <= 16:
+        gen2 = torch.Generator().manual_seed(11)
+        xqa2 = Xqa(max_batch=w0.batch, num_q_heads=w0.num_q_heads, num_kv_heads=w0.num_kv_heads,
+                   max_pages_per_seq=w0.max_pages_per_seq, max_query_tokens=2)
+        q2 = [torch.randn((w.batch, 2, w.num_q_heads, w.head_dim), generator=gen2).half().to(dev)
+              for w in works]
+        out2 = [torch.empty_like(x) for x in q2]
+
+        def call2(i):
+            d = devs[i]
+            xqa2.decode(q=q2[i], k_pages=d.k_pages, v_pages=d.v_pages, block_table=d.block_table,
+                        context_lens=d.context_lens, scale=w0.scale, out=out2[i])
+
+        for i in range(R):
+            call2(i)
+        torch.cuda.synchronize()
+        multi2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(multi2):
+            for i in range(R):
+                call2(i)
+        for _ in range(max(args.warmup // R, 2)):
+            multi2.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps // R):
+            multi2.replay()
+        torch.cuda.synchronize()
+        us_m2 = (time.perf_counter() - t) / steps * 1e6
+        detail["multi_token"] = {"tokens_per_sequence": 2, "us_per_step_graph_Rstep": us_m2,
+                                 "ratio_to_one_token": us_m2 / us_step}
+        log(f"two query tokens per sequence: {us_m2:.2f} us/step ({us_m2 / us_step:.3f}x one token)")
+        xqa2.close()
 
     # ------------------------------------------------------------ KV append
     # The step before decode in serving: each sequence's new token written

@@ -13,7 +13,8 @@ XQA_ERR_OUT_OF_MEMORY = 3
 XQA_ERR_HIP = 4
 
 EXPORTED = [
-    "xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_split",
+    "xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_multi",
+    "xqa_decode_split",
     "xqa_decode_combine", "xqa_append_kv", "xqa_plan", "xqa_debug_widen_e5m2",
     "xqa_status_string", "xqa_last_error",
 ]
@@ -28,6 +29,7 @@ class XqaConfig(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32),
         ("max_work_items", ctypes.c_int32),
+        ("max_query_tokens", ctypes.c_int32),
     ]
 
 
@@ -68,6 +70,7 @@ def load() -> ctypes.CDLL:
     lib.xqa_get_info.argtypes = [vp, ctypes.POINTER(XqaInfo)]
     dec = [vp, vp, vp, vp, vp, vp, i32, f32, vp, vp]
     lib.xqa_decode.argtypes = dec
+    lib.xqa_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp]
     lib.xqa_decode_split.argtypes = dec
     lib.xqa_decode_combine.argtypes = [vp, vp, i32, vp, vp]
     lib.xqa_append_kv.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp]
@@ -77,7 +80,8 @@ def load() -> ctypes.CDLL:
     lib.xqa_status_string.restype = ctypes.c_char_p
     lib.xqa_last_error.argtypes = []
     lib.xqa_last_error.restype = ctypes.c_char_p
-    for name in ("xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_split",
+    for name in ("xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_multi",
+                 "xqa_decode_split",
                  "xqa_decode_combine", "xqa_append_kv", "xqa_plan", "xqa_debug_widen_e5m2"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib

@@ -42,12 +42,13 @@ class Xqa:
 
     def __init__(self, *, max_batch: int, num_q_heads: int, num_kv_heads: int,
                  max_pages_per_seq: int, head_dim: int = HEAD_DIM, page_size: int = PAGE_SIZE,
-                 max_work_items: int = 0, device: Optional[torch.device] = None):
+                 max_work_items: int = 0, max_query_tokens: int = 1,
+                 device: Optional[torch.device] = None):
         lib = _lib.load()
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
             else torch.device(device)
         cfg = _lib.XqaConfig(max_batch, num_q_heads, num_kv_heads, head_dim, page_size,
-                             max_pages_per_seq, max_work_items)
+                             max_pages_per_seq, max_work_items, max_query_tokens)
         handle = ctypes.c_void_p()
         with torch.cuda.device(self.device):
             _lib.check(lib.xqa_create(ctypes.byref(cfg), ctypes.byref(handle)))
@@ -56,6 +57,7 @@ class Xqa:
         self.num_q_heads = num_q_heads
         self.num_kv_heads = num_kv_heads
         self.max_pages_per_seq = max_pages_per_seq
+        self.max_query_tokens = max_query_tokens
         self.head_dim = head_dim
         self.page_size = page_size
 
@@ -86,10 +88,17 @@ class Xqa:
             _need(t.device == dev, f"{name} must be on {dev}, got {t.device}")
             _need(t.is_contiguous(), f"{name} must be contiguous")
         Hq, Hkv, D, P = self.num_q_heads, self.num_kv_heads, self.head_dim, self.page_size
-        _need(q.dim() == 3 and q.shape[1:] == (Hq, D) and q.shape[0] >= batch,
-              f"q must be [>= batch, {Hq}, {D}], got {tuple(q.shape)}")
-        _need(out.dim() == 3 and out.shape[1:] == (Hq, D) and out.shape[0] >= batch,
-              f"out must be [>= batch, {Hq}, {D}], got {tuple(out.shape)}")
+        if q.dim() == 4:   # [batch, M, Hq, D]: several query tokens per sequence
+            _need(q.shape[2:] == (Hq, D) and q.shape[0] >= batch
+                  and 1 <= q.shape[1] <= self.max_query_tokens,
+                  f"q must be [>= batch, 1..{self.max_query_tokens}, {Hq}, {D}], got {tuple(q.shape)}")
+            _need(out.dim() == 4 and out.shape[1:] == q.shape[1:] and out.shape[0] >= batch,
+                  f"out must be [>= batch, {q.shape[1]}, {Hq}, {D}], got {tuple(out.shape)}")
+        else:
+            _need(q.dim() == 3 and q.shape[1:] == (Hq, D) and q.shape[0] >= batch,
+                  f"q must be [>= batch, {Hq}, {D}], got {tuple(q.shape)}")
+            _need(out.dim() == 3 and out.shape[1:] == (Hq, D) and out.shape[0] >= batch,
+                  f"out must be [>= batch, {Hq}, {D}], got {tuple(out.shape)}")
         _need(k_pages.dim() == 4 and k_pages.shape[1:] == (Hkv, P, D),
               f"k_pages must be [num_pages, {Hkv}, {P}, {D}], got {tuple(k_pages.shape)}")
         _need(v_pages.shape == k_pages.shape, "v_pages must have k_pages' shape")
@@ -117,14 +126,22 @@ class Xqa:
                block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                out: Optional[torch.Tensor] = None, batch: Optional[int] = None,
                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-        """One decode step (split kernel + combine kernel) on the current stream."""
+        """One decode step (split kernel + combine kernel) on the current stream.
+
+        q is [B, Hq, D] (one new token per sequence, xqa_decode) or
+        [B, M, Hq, D] (M new tokens, causal among themselves,
+        xqa_decode_multi); out has q's shape."""
         out, args = self._args(q, k_pages, v_pages, block_table, context_lens, out, batch, scale, stream)
-        _lib.check(_lib.load().xqa_decode(*args))
+        if q.dim() == 4:
+            _lib.check(_lib.load().xqa_decode_multi(*args[:7], int(q.shape[1]), *args[7:]))
+        else:
+            _lib.check(_lib.load().xqa_decode(*args))
         return out
 
     def split(self, *, q, k_pages, v_pages, block_table, context_lens, scale, out=None,
               batch=None, stream=None) -> torch.Tensor:
-        """First stage only (xqa_decode_split); combine() must follow."""
+        """First stage only (xqa_decode_split, one query token); combine() must follow."""
+        _need(isinstance(q, torch.Tensor) and q.dim() == 3, "split() takes q [B, Hq, D]")
         out, args = self._args(q, k_pages, v_pages, block_table, context_lens, out, batch, scale, stream)
         _lib.check(_lib.load().xqa_decode_split(*args))
         return out

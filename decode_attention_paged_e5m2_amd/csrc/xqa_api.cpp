@@ -71,7 +71,8 @@ xqa_status_t check_device(xqa_handle_t h) {
 
 xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_pages,
                             const uint8_t* v_pages, const int32_t* block_table,
-                            const int32_t* context_lens, int32_t batch, float scale, void* out) {
+                            const int32_t* context_lens, int32_t batch, float scale, void* out,
+                            int32_t q_tokens = 1) {
   xqa::AttendArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k_pages = k_pages;
@@ -83,6 +84,8 @@ xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_page
   a.batch = batch;
   a.num_kv_heads = h->cfg.num_kv_heads;
   a.group = h->cfg.num_q_heads / h->cfg.num_kv_heads;
+  a.q_tokens = q_tokens;
+  a.rows = a.group * q_tokens;
   a.max_pages = h->cfg.max_pages_per_seq;
   a.max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
   a.per_head = h->per_head;
@@ -111,7 +114,7 @@ const char* xqa_last_error(void) { return g_last_error; }
 xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
   if (!cfg || !out_handle) return fail(XQA_ERR_INVALID_ARG, "null cfg or out_handle");
   if (cfg->max_batch < 1 || cfg->num_q_heads < 1 || cfg->num_kv_heads < 1 ||
-      cfg->max_pages_per_seq < 1 || cfg->max_work_items < 0)
+      cfg->max_pages_per_seq < 1 || cfg->max_work_items < 0 || cfg->max_query_tokens < 0)
     return fail(XQA_ERR_INVALID_ARG, "sizes must be positive");
   if (cfg->head_dim != xqa::kHeadDim) return fail(XQA_ERR_UNSUPPORTED, "head_dim must be 128");
   if (cfg->page_size != xqa::kPageSize) return fail(XQA_ERR_UNSUPPORTED, "page_size must be 16");
@@ -119,6 +122,10 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
     return fail(XQA_ERR_UNSUPPORTED, "num_q_heads must be a multiple of num_kv_heads");
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
   if (G > xqa::kMaxGroup) return fail(XQA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+  const int max_q = cfg->max_query_tokens == 0 ? 1 : cfg->max_query_tokens;
+  if ((long long)G * max_q > xqa::kMaxGroup)
+    return fail(XQA_ERR_UNSUPPORTED,
+                "query heads per KV head times max_query_tokens must not exceed 16");
   if (cfg->max_batch > xqa::kMaxBatch) return fail(XQA_ERR_UNSUPPORTED, "max_batch above 65536");
   if ((long long)cfg->max_pages_per_seq * xqa::kPageSize > xqa::kMaxSeqTokens)
     return fail(XQA_ERR_UNSUPPORTED, "max_pages_per_seq * page_size must not exceed 2^24 tokens");
@@ -149,13 +156,15 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
   }
   const int per_head = (int)(grid / cfg->num_kv_heads);
   grid = (long long)per_head * cfg->num_kv_heads;
-  const int stride = ((G * (xqa::kHeadDim + 2)) + 3) / 4 * 4;
+  // A record holds O, max and sum of every query row: G * max_query_tokens rows.
+  const int stride = ((G * max_q * (xqa::kHeadDim + 2)) + 3) / 4 * 4;
   // Two record slots per work item: its first and its last segment.
   const size_t ws = (size_t)2 * grid * stride * sizeof(float);
 
   xqa_handle_s* h = new (std::nothrow) xqa_handle_s();
   if (!h) return fail(XQA_ERR_OUT_OF_MEMORY, "host allocation failed");
   h->cfg = *cfg;
+  h->cfg.max_query_tokens = max_q;
   h->device = dev;
   h->grid = (int)grid;
   h->per_head = per_head;
@@ -230,12 +239,22 @@ xqa_status_t xqa_decode(xqa_handle_t h, const void* q, const uint8_t* k_pages,
                         const uint8_t* v_pages, const int32_t* block_table,
                         const int32_t* context_lens, int32_t batch, float scale, void* out,
                         void* stream) {
+  return xqa_decode_multi(h, q, k_pages, v_pages, block_table, context_lens, batch, 1, scale, out,
+                          stream);
+}
+
+xqa_status_t xqa_decode_multi(xqa_handle_t h, const void* q, const uint8_t* k_pages,
+                              const uint8_t* v_pages, const int32_t* block_table,
+                              const int32_t* context_lens, int32_t batch, int32_t num_query_tokens,
+                              float scale, void* out, void* stream) {
   xqa_status_t st =
       check_decode_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
   if (st != XQA_OK) return st;
+  if (num_query_tokens < 1 || num_query_tokens > h->cfg.max_query_tokens)
+    return fail(XQA_ERR_INVALID_ARG, "num_query_tokens outside [1, max_query_tokens]");
   if ((st = check_device(h)) != XQA_OK) return st;
-  const xqa::AttendArgs a =
-      attend_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
+  const xqa::AttendArgs a = attend_args(h, q, k_pages, v_pages, block_table, context_lens, batch,
+                                        scale, out, num_query_tokens);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = xqa::launch_split(a, h->grid, s);
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");

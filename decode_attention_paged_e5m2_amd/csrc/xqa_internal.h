@@ -74,6 +74,8 @@ struct AttendArgs {
   int32_t batch;
   int32_t num_kv_heads;
   int32_t group;
+  int32_t q_tokens;       // M new query tokens per sequence (1: single-token decode)
+  int32_t rows;           // G * M <= 16: the MFMA N dimension, row r = (token r / G, head r % G)
   int32_t max_pages;
   int32_t max_tokens;
   int32_t per_head;       // grid / Hkv

@@ -255,12 +255,16 @@ __device__ __forceinline__ void load_block(RawBlock& r, const uint8_t* ka, const
 
 // kTail: the block may extend past t_end (only a wave's last block of a
 // segment can); other blocks skip the masking.
+// t_end: end of the segment's tokens (V rows past it are zeroed). row_end:
+// this lane's query row sees tokens < row_end (<= t_end; smaller for the
+// earlier of several query tokens). t_mask: the smallest row_end of the wave.
 template <bool kTail>
 __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4], WaveState& st,
-                                              float scale_log2e, int tok0, int t_end, int lane,
-                                              uint32_t sel1, uint32_t selh0, uint32_t selh1) {
+                                              float scale_log2e, int tok0, int t_end, int row_end,
+                                              int t_mask, int lane, uint32_t sel1, uint32_t selh0,
+                                              uint32_t selh1) {
   const int q = lane >> 4;
-  const bool tail = kTail && tok0 + kBlockTokens > t_end;   // wave-uniform
+  const bool tail = kTail && tok0 + kBlockTokens > t_mask;   // wave-uniform
   if (tail) {
     // V rows of tokens past the end are zeroed (their bytes may be NaN codes
     // and 0 * NaN would poison the sum). V lane token: 4q + (lane & 3).
@@ -304,8 +308,8 @@ __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4],
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int t = tok0 + 4 * q + r4;
-      s8[r4] = t >= t_end ? -INFINITY : s8[r4] * scale_log2e;
-      s8[4 + r4] = t + kPageSize >= t_end ? -INFINITY : s8[4 + r4] * scale_log2e;
+      s8[r4] = t >= row_end ? -INFINITY : s8[r4] * scale_log2e;
+      s8[4 + r4] = t + kPageSize >= row_end ? -INFINITY : s8[4 + r4] * scale_log2e;
     }
     bm = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])),
                fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
@@ -326,7 +330,8 @@ __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4],
   // reference gives the same softmax; the merges below use it as such.
   if (__any(bm > st.m + kRescaleSlack)) {
     const float m_new = fmaxf(st.m, bm);
-    const float alpha = exp2_fast(st.m - m_new);
+    // Equal maxima (both -inf for a row that has seen no visible token) keep the state.
+    const float alpha = st.m == m_new ? 1.f : exp2_fast(st.m - m_new);
     st.m = m_new;
 #pragma unroll
     for (int t = 0; t < 8; ++t) st.o[t] *= alpha;
@@ -336,9 +341,12 @@ __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4],
 
   u32x4 pf;
   if (tail) {
+    // A masked score is -inf; so is m_ref for a row with nothing visible yet.
 #pragma unroll
     for (int r2 = 0; r2 < 4; ++r2) {
-      pf[r2] = pack_half2(exp2_fast(s8[2 * r2] - m_ref), exp2_fast(s8[2 * r2 + 1] - m_ref));
+      const float p0 = s8[2 * r2] == -INFINITY ? 0.f : exp2_fast(s8[2 * r2] - m_ref);
+      const float p1 = s8[2 * r2 + 1] == -INFINITY ? 0.f : exp2_fast(s8[2 * r2 + 1] - m_ref);
+      pf[r2] = pack_half2(p0, p1);
     }
   } else {
 #pragma unroll
@@ -371,6 +379,14 @@ __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4],
   }
 }
 
+// Output row of query row r (token r / G, head h * G + r % G) of sequence b:
+// out is [batch][M][Hq][head_dim].
+__device__ __forceinline__ uint16_t* out_row(const AttendArgs& a, int b, int h, int r) {
+  const int G = a.group;
+  return a.out + (((long long)b * a.q_tokens + r / G) * a.num_kv_heads * G + (long long)h * G + r % G) *
+                     kHeadDim;
+}
+
 struct SplitShared {
   float m[kWaves][kMaxGroup];
   float l[kWaves][kMaxGroup];
@@ -385,17 +401,23 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
                                             int n, int jb_lo, int jb_hi, bool direct, float* rec,
                                             int lane, int wave) {
   const int G = a.group;
+  const int R = a.rows;
+  const int M = a.q_tokens;
   const int Hkv = a.num_kv_heads;
   const int t_begin = jb_lo * kBlockTokens;
   const int t_end = min(n, jb_hi * kBlockTokens);
-  const int g = lane & 15;
+  const int g = lane & 15;   // query row: token g / G, head h * G + g % G
   const int q = lane >> 4;
+  // Query token j sits at position n - M + j and sees tokens <= n - M + j.
+  const int row_end = min(t_end, n - M + g / G + 1);
+  const int t_mask = min(t_end, n - M + 1);
 
-  // Q^T fragments: lane (head g, quarter q) holds, for MFMA i, the eight
+  // Q^T fragments: lane (row g, quarter q) holds, for MFMA i, the eight
   // head-dim values 64*(i/2) + 16q + 8*(i%2) + 0..7, matching the K bytes.
   half8 qf[4];
-  if (g < G) {
-    const uint16_t* qrow = a.q + ((long long)b * Hkv * G + (long long)h * G + g) * kHeadDim;
+  if (g < R) {
+    const uint16_t* qrow = a.q + (((long long)b * M + g / G) * Hkv * G + (long long)h * G + g % G) *
+                                     kHeadDim;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       qf[i] = *(const half8*)(qrow + 64 * (i >> 1) + 16 * q + 8 * (i & 1));
@@ -451,21 +473,26 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
     int mm = 0;
     for (; mm + 2 < cnt; mm += 2) {
       issue(B, mm + 1);
-      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
+      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
+                           selh0, selh1);
       issue(A, mm + 2);
-      process_block<false>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
+      process_block<false>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, row_end, t_mask, lane,
+                           sel1, selh0, selh1);
     }
     if (cnt - mm == 2) {
       issue(B, mm + 1);
-      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
-      process_block<true>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, lane, sel1, selh0, selh1);
+      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
+                           selh0, selh1);
+      process_block<true>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, row_end, t_mask, lane,
+                          sel1, selh0, selh1);
     } else {
-      process_block<true>(A, qf, st, a.scale_log2e, tok0(mm), t_end, lane, sel1, selh0, selh1);
+      process_block<true>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
+                          selh0, selh1);
     }
   }
 
   // Publish the wave's state.
-  if (g < G) {
+  if (g < R) {
     if (q == 0) {
       sh.m[wave][g] = st.m;
       sh.l[wave][g] = st.l[0];
@@ -481,8 +508,7 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
   __syncthreads();
 
   // Merge the four waves (fixed order): the segment's (max, sum, O).
-  uint16_t* out_group = a.out + ((long long)b * Hkv * G + (long long)h * G) * kHeadDim;
-  for (int e = threadIdx.x; e < G * 32; e += kThreads) {
+  for (int e = threadIdx.x; e < R * 32; e += kThreads) {
     const int gg = e >> 5;
     const int d4 = (e & 31) * 4;
     float M = sh.m[0][gg];
@@ -498,16 +524,16 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
       o += f * *(const float4v*)&sh.o[w][gg][d4];
     }
     if (direct) {
-      const float inv = 1.0f / Ls;
+      const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;   // a row with no visible token is zero
       uint2 packed;
       packed.x = pack_half2(o[0] * inv, o[1] * inv);
       packed.y = pack_half2(o[2] * inv, o[3] * inv);
-      *(uint2*)(out_group + gg * kHeadDim + d4) = packed;
+      *(uint2*)(out_row(a, b, h, gg) + d4) = packed;
     } else {
       *(float4v*)(rec + gg * kHeadDim + d4) = o;
       if (d4 == 0) {
-        rec[G * kHeadDim + gg] = M;
-        rec[G * kHeadDim + G + gg] = Ls;
+        rec[R * kHeadDim + gg] = M;
+        rec[R * kHeadDim + R + gg] = Ls;
       }
     }
   }
@@ -556,22 +582,22 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
 // (one for most sequences) and no cross-lane reduction.
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) {
   const int lane = threadIdx.x & 63;
-  const int G = a.group;
+  const int R = a.rows;
   const int Hkv = a.num_kv_heads;
   const int chunk = blockIdx.x % kCombineChunks;
   const int bh = blockIdx.x / kCombineChunks;
   const int b = bh / Hkv;
   const int h = bh % Hkv;
   constexpr int kCols = kHeadDim / kCombineChunks;   // 16 columns per chunk
+  constexpr int kPairs = kCols / 2;                  // lanes per query row
 
   const SeqTable seqs(a.context_lens, a.batch, a.max_tokens, lane);
   const long long NB = seqs.nb;
   const int P = items_per_head(NB, a.per_head);
   const SeqInfo sq = seqs.at(b, lane);
-  uint16_t* out_group = a.out + ((long long)b * Hkv * G + (long long)h * G) * kHeadDim;
   if (sq.n == 0) {
-    for (int e = threadIdx.x; e < G * kCols / 2; e += kCombineThreads) {
-      *(uint32_t*)(out_group + (e / (kCols / 2)) * kHeadDim + chunk * kCols + (e % (kCols / 2)) * 2) = 0;
+    for (int e = threadIdx.x; e < R * kPairs; e += kCombineThreads) {
+      *(uint32_t*)(out_row(a, b, h, e / kPairs) + chunk * kCols + (e % kPairs) * 2) = 0;
     }
     return;
   }
@@ -581,15 +607,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) 
   // Item i0 holds this sequence in slot 2*i0 if the sequence starts its
   // block range, else in slot 2*i0 + 1; later items hold it in slot 2*i.
   const int slot0 = (sq.off == item_lo(i0, NB, P)) ? 2 * i0 : 2 * i0 + 1;
-  const int mo = G * kHeadDim;
+  const int mo = R * kHeadDim;
   auto rec = [&](int s) {
     const int slot = s == 0 ? slot0 : 2 * (i0 + s);
     return a.partials + ((long long)slot * Hkv + h) * a.item_stride;
   };
 
-  for (int e = threadIdx.x; e < G * kCols / 2; e += kCombineThreads) {
-    const int gg = e / (kCols / 2);
-    const int col = gg * kHeadDim + chunk * kCols + (e % (kCols / 2)) * 2;
+  for (int e = threadIdx.x; e < R * kPairs; e += kCombineThreads) {
+    const int gg = e / kPairs;
+    const int c = chunk * kCols + (e % kPairs) * 2;   // first of this lane's two columns
+    const int col = gg * kHeadDim + c;
     float M = -INFINITY, Ls = 0.f;
     float o0 = 0.f, o1 = 0.f;
     for (int s0 = 0; s0 < nsb; s0 += kCombineRound) {
@@ -603,26 +630,28 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) 
         const float* r = rec(min(s0 + k, nsb - 1));
         ov[k] = *(const float2*)(r + col);
         mv[k] = r[mo + gg];
-        lv[k] = r[mo + G + gg];
+        lv[k] = r[mo + R + gg];
       }
       float mr = M;
 #pragma unroll
       for (int k = 0; k < kCombineRound; ++k) mr = fmaxf(mr, k < cnt ? mv[k] : -INFINITY);
-      const float fa = exp2_fast(M - mr);   // rescales earlier rounds (0 on the first)
+      // Rescales earlier rounds (0 on the first). A state of a query row
+      // that saw no token has m = -inf and weight 0; equal maxima keep the sums.
+      const float fa = M == mr ? 1.f : exp2_fast(M - mr);
       Ls *= fa;
       o0 *= fa;
       o1 *= fa;
       M = mr;
 #pragma unroll
       for (int k = 0; k < kCombineRound; ++k) {
-        const float w = k < cnt ? exp2_fast(mv[k] - M) : 0.f;
+        const float w = (k < cnt && mv[k] != -INFINITY) ? exp2_fast(mv[k] - M) : 0.f;
         Ls += w * lv[k];
         o0 += w * ov[k].x;
         o1 += w * ov[k].y;
       }
     }
-    const float inv = 1.0f / Ls;
-    *(uint32_t*)(out_group + col) = pack_half2(o0 * inv, o1 * inv);
+    const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;   // a row with no visible token is zero
+    *(uint32_t*)(out_row(a, b, h, gg) + c) = pack_half2(o0 * inv, o1 * inv);
   }
 }
 

@@ -69,6 +69,8 @@ typedef struct {
   int32_t max_pages_per_seq; /* >= 1: block-table row stride in int32 elements          */
   int32_t max_work_items;    /* 0: sized from the device's occupancy; else the split    */
                              /* grid in workgroups, in [Hkv, Hkv*2048]                  */
+  int32_t max_query_tokens;  /* 0 or 1: one query token per sequence; up to M with      */
+                             /* G * M <= 16 for xqa_decode_multi                        */
 } xqa_config_t;
 
 typedef struct {
@@ -86,7 +88,8 @@ typedef struct {
  * split states (the only allocation the library makes). *out_handle is set
  * only on XQA_OK. Errors: INVALID_ARG (null pointers, non-positive sizes),
  * UNSUPPORTED (head_dim != 128, page_size != 16, Hq % Hkv != 0, G > 16,
- * max_batch > 65536, more than 2^24 tokens per sequence),
+ * G * max_query_tokens > 16, max_batch > 65536, more than 2^24 tokens per
+ * sequence),
  * OUT_OF_MEMORY, HIP (no device). */
 xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle);
 
@@ -110,6 +113,23 @@ xqa_status_t xqa_decode(xqa_handle_t handle, const void* q, const uint8_t* k_pag
                         const uint8_t* v_pages, const int32_t* block_table,
                         const int32_t* context_lens, int32_t batch, float scale,
                         void* out, void* stream);
+
+/* Several new query tokens per sequence (speculative or multi-token
+ * prediction rows, which the page "[Kernel][SM70] Pipeline batched E5M2 XQA
+ * decode" lists beside single-token decode in its Purpose), causal among
+ * themselves. q and out are binary16 [batch][M][Hq][head_dim], M =
+ * num_query_tokens in [1, max_query_tokens]. With n as for xqa_decode (it
+ * counts the M new tokens), query token j sits at position n - M + j:
+ *     out[b][j][hq][:] = attention of q[b][j][hq] over tokens 0 .. n - M + j
+ * and is a zero row when n - M + j < 0. The G * M query rows of a KV head
+ * share one pass over its pages (they fill the matrix-core tile that a single
+ * token leaves half empty at G = 8), so M = 2 reads the same KV bytes as
+ * M = 1. M = 1 is exactly xqa_decode. Other arguments, alignment and errors
+ * as for xqa_decode; INVALID_ARG also for num_query_tokens out of range. */
+xqa_status_t xqa_decode_multi(xqa_handle_t handle, const void* q, const uint8_t* k_pages,
+                              const uint8_t* v_pages, const int32_t* block_table,
+                              const int32_t* context_lens, int32_t batch, int32_t num_query_tokens,
+                              float scale, void* out, void* stream);
 
 /* First stage of xqa_decode alone (device-side plan, page gather, widening,
  * QK, online softmax, PV): rows of sequences that fit one work item are

@@ -55,6 +55,8 @@ def _cfg(**over):
     (dict(num_q_heads=68, num_kv_heads=4), 2), (dict(max_batch=0), 1),
     (dict(max_pages_per_seq=0), 1), (dict(max_work_items=3), 1), (dict(max_work_items=9000), 1),
     (dict(max_batch=70000), 2), (dict(max_pages_per_seq=(1 << 20) + 1), 2),
+    (dict(max_query_tokens=-1), 1), (dict(max_query_tokens=3), 2),
+    (dict(num_q_heads=4, num_kv_heads=4, max_query_tokens=17), 2),
 ])
 def test_create_rejects_bad_configs_before_hip(lib, over, status):
     h = ctypes.c_void_p()
@@ -71,6 +73,7 @@ def test_null_arguments_are_rejected(lib):
     args = [null] * 6 + [1, ctypes.c_float(0.1), null, null]
     assert lib.xqa_decode(*args) == 1
     assert lib.xqa_decode_split(*args) == 1
+    assert lib.xqa_decode_multi(*args[:7], 2, *args[7:]) == 1
     assert lib.xqa_decode_combine(null, null, 1, null, null) == 1
     assert lib.xqa_append_kv(null, null, null, null, null, 1, null, null, null) == 1
     assert lib.xqa_get_info(null, None) == 1
