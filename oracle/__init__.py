@@ -29,6 +29,9 @@ All arithmetic is float64 numpy. Functions:
 * ``attention.decode_attention_row``  one (sequence, query head) row
 * ``attention.decode_attention_multi``  M new query tokens per sequence,
   causal among themselves
+* ``e4m3.decode_e4m3``          closed-form OCP E4M3 code -> float64
+* ``attention.decode_attention_fp8``  the operation over an E5M2 or E4M3
+  cache with per-tensor K and V dequantisation scales
 * ``attention.partial_state`` / ``attention.merge_states``  the split-context
   form (running max, sum of weights, unnormalised output) and its
   log-sum-exp merge, used to pin the split-K + combine arithmetic.
@@ -44,9 +47,11 @@ pure-Python brute force on tiny shapes; split-and-merge equals single pass.
 """
 
 from .e5m2 import decode_e5m2, E5M2_TABLE, E5M2_MAX_FINITE
+from .e4m3 import decode_e4m3, E4M3_TABLE, E4M3_MAX_FINITE
 from .append import encode_e5m2, append_kv
 from .attention import (
     decode_attention,
+    decode_attention_fp8,
     decode_attention_multi,
     decode_attention_row,
     gather_tokens,
@@ -66,4 +71,8 @@ __all__ = [
     "merge_states",
     "encode_e5m2",
     "append_kv",
+    "decode_e4m3",
+    "E4M3_TABLE",
+    "E4M3_MAX_FINITE",
+    "decode_attention_fp8",
 ]

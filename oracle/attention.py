@@ -168,3 +168,47 @@ def decode_attention_multi(q, k_pages, v_pages, block_table, context_lens, scale
                 W = np.exp(Z - Z.max(axis=1, keepdims=True))
                 out[b, j, h * G:(h + 1) * G, :] = (W @ V) / W.sum(axis=1, keepdims=True)
     return out
+
+
+def decode_attention_fp8(q, k_pages, v_pages, block_table, context_lens, scale, *,
+                         kv_format="e5m2", k_scale=1.0, v_scale=1.0) -> np.ndarray:
+    """Decode over an FP8 cache with per-tensor dequantisation scales: float64.
+
+    q is [B, Hq, D] (one query token per sequence) or [B, M, Hq, D] (M tokens,
+    causal as in decode_attention_multi); the output has q's shape. kv_format
+    is "e5m2" or "e4m3"; the cached K and V values are k_scale * dec(code) and
+    v_scale * dec(code) (k_scale and v_scale cross the boundary as fp32).
+    Reading taken: one scale per tensor (all pages, heads and tokens), as
+    the "per-tensor scales" variant names.
+    """
+    from .e4m3 import E4M3_TABLE
+    table = {"e5m2": E5M2_TABLE, "e4m3": E4M3_TABLE}[kv_format]
+    q = np.asarray(q)
+    single = q.ndim == 3
+    q4 = q[:, None] if single else q
+    B, M, Hq, D = q4.shape
+    Hkv = k_pages.shape[1]
+    P = k_pages.shape[2]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    s64 = _as_f64_scale(scale)
+    ks = float(np.float32(k_scale))
+    vs = float(np.float32(v_scale))
+    out = np.zeros((B, M, Hq, D), dtype=np.float64)
+    for b in range(B):
+        n = _effective_len(context_lens, block_table, P, b)
+        for j in range(M):
+            visible = n - M + j + 1
+            if visible <= 0:
+                continue
+            t = np.arange(visible)
+            pages = block_table[b, t // P].astype(np.int64)
+            for h in range(Hkv):
+                K = ks * table[k_pages[pages, h, t % P, :]]
+                V = vs * table[v_pages[pages, h, t % P, :]]
+                Qg = np.asarray(q4[b, j, h * G:(h + 1) * G, :], dtype=np.float64)
+                Z = s64 * (Qg @ K.T)
+                W = np.exp(Z - Z.max(axis=1, keepdims=True))
+                out[b, j, h * G:(h + 1) * G, :] = (W @ V) / W.sum(axis=1, keepdims=True)
+    return out[:, 0] if single else out
