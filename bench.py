@@ -16,9 +16,10 @@ independent warm-up of each arm -> timed replays of one graph holding R
 consecutive steps (the headline; one-step-per-graph replays are reported too) ->
 A/B/B/A eager vs graph blocks -> per-launch HIP-event timing of the split
 kernel (the dominant one) and of the combine kernel on the stream they are
-launched on -> two query tokens per sequence (xqa_decode_multi) and the KV
-append (xqa_append_kv) per launch and in a graph of append + decode steps,
-reported in detail. Prints one JSON line.
+launched on -> two query tokens per sequence (xqa_decode_multi), the same
+workload as an E4M3 cache with per-tensor scales (xqa_decode_fp8), and the
+KV append (xqa_append_kv) per launch and in a graph of append + decode
+steps, reported in detail. Prints one JSON line.
 """
 
 import argparse
@@ -357,6 +358,41 @@ def main():
                                  "ratio_to_one_token": us_m2 / us_step}
         log(f"two query tokens per sequence: {us_m2:.2f} us/step ({us_m2 / us_step:.3f}x one token)")
         xqa2.close()
+
+    # ------------------------------------------------------------ E4M3 cache
+    # The same workload with its K/V quantised to E4M3 and per-tensor scales
+    # (xqa_decode_fp8): same bytes per step, a different widening.
+    works4 = [make_config(args.config, v, kv_format="e4m3") for v in range(R)]
+    devs4 = [to_device(w, dev) for w in works4]
+    out4 = [torch.empty_like(d.q) for d in devs4]
+
+    def call4(i):
+        d = devs4[i]
+        xqa.decode(q=d.q, k_pages=d.k_pages, v_pages=d.v_pages, block_table=d.block_table,
+                   context_lens=d.context_lens, scale=w0.scale, out=out4[i], kv_format="e4m3",
+                   k_scale=0.5, v_scale=2.0)
+
+    for i in range(R):
+        call4(i)
+    torch.cuda.synchronize()
+    graph4 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph4):
+        for i in range(R):
+            call4(i)
+    for _ in range(max(args.warmup // R, 2)):
+        graph4.replay()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps // R):
+        graph4.replay()
+    torch.cuda.synchronize()
+    us_e4 = (time.perf_counter() - t) / steps * 1e6
+    bytes4 = statistics.mean(w.kv_bytes for w in works4)
+    detail["e4m3_scaled"] = {"us_per_step_graph_Rstep": us_e4, "kv_gbs": bytes4 / us_e4 / 1e3,
+                             "ratio_to_e5m2": us_e4 / us_step}
+    log(f"E4M3 cache with scales: {us_e4:.2f} us/step ({us_e4 / us_step:.3f}x E5M2)")
+    del graph4, devs4, out4, works4
+    torch.cuda.synchronize()
 
     # ------------------------------------------------------------ KV append
     # The step before decode in serving: each sequence's new token written

@@ -5,6 +5,6 @@ declared in include/xqa.h); this package loads it and marshals arguments.
 """
 
 from ._lib import LIB_PATH, XqaError, load as load_library
-from .binding import Xqa, debug_widen_e5m2
+from .binding import Xqa, debug_widen_e4m3, debug_widen_e5m2
 
-__all__ = ["Xqa", "debug_widen_e5m2", "XqaError", "load_library", "LIB_PATH"]
+__all__ = ["Xqa", "debug_widen_e5m2", "debug_widen_e4m3", "XqaError", "load_library", "LIB_PATH"]

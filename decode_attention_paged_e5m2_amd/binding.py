@@ -30,6 +30,9 @@ def _need(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
+_KV_FORMATS = {"e5m2": 0, "e4m3": 1}   # xqa_kv_format_t
+
+
 class Xqa:
     """A decode-attention handle: fixed head counts, capacity and workspace.
 
@@ -125,17 +128,27 @@ class Xqa:
     def decode(self, *, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
                block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                out: Optional[torch.Tensor] = None, batch: Optional[int] = None,
+               kv_format: str = "e5m2", k_scale: float = 1.0, v_scale: float = 1.0,
                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
         """One decode step (split kernel + combine kernel) on the current stream.
 
         q is [B, Hq, D] (one new token per sequence, xqa_decode) or
         [B, M, Hq, D] (M new tokens, causal among themselves,
-        xqa_decode_multi); out has q's shape."""
+        xqa_decode_multi); out has q's shape. kv_format "e4m3" or scales
+        other than 1 go through xqa_decode_fp8."""
+        _need(kv_format in _KV_FORMATS, f"kv_format must be one of {sorted(_KV_FORMATS)}")
         out, args = self._args(q, k_pages, v_pages, block_table, context_lens, out, batch, scale, stream)
-        if q.dim() == 4:
-            _lib.check(_lib.load().xqa_decode_multi(*args[:7], int(q.shape[1]), *args[7:]))
+        M = int(q.shape[1]) if q.dim() == 4 else 1
+        lib = _lib.load()
+        if kv_format != "e5m2" or k_scale != 1.0 or v_scale != 1.0:
+            _need(math.isfinite(k_scale) and math.isfinite(v_scale), "scales must be finite")
+            _lib.check(lib.xqa_decode_fp8(args[0], _KV_FORMATS[kv_format], *args[1:7], M, args[7],
+                                          ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+                                          *args[8:]))
+        elif q.dim() == 4:
+            _lib.check(lib.xqa_decode_multi(*args[:7], M, *args[7:]))
         else:
-            _lib.check(_lib.load().xqa_decode(*args))
+            _lib.check(lib.xqa_decode(*args))
         return out
 
     def split(self, *, q, k_pages, v_pages, block_table, context_lens, scale, out=None,
@@ -214,15 +227,24 @@ class Xqa:
             pass
 
 
+def _debug_widen(fn, codes, stream):
+    _need(codes.dtype == torch.uint8 and codes.is_cuda and codes.is_contiguous(),
+          "codes must be a contiguous uint8 GPU tensor")
+    bits = torch.empty(codes.shape, dtype=torch.int16, device=codes.device)
+    vals = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    _lib.check(fn(_ptr(codes), _ptr(bits), _ptr(vals), codes.numel(),
+                  _stream_ptr(stream, codes.device)))
+    return bits, vals
+
+
 def debug_widen_e5m2(codes: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
     """Widen uint8 E5M2 codes on the GPU with the kernels' own routine.
 
     Returns (binary16 bit patterns as int16, values as float32).
     """
-    _need(codes.dtype == torch.uint8 and codes.is_cuda and codes.is_contiguous(),
-          "codes must be a contiguous uint8 GPU tensor")
-    bits = torch.empty(codes.shape, dtype=torch.int16, device=codes.device)
-    vals = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
-    _lib.check(_lib.load().xqa_debug_widen_e5m2(_ptr(codes), _ptr(bits), _ptr(vals), codes.numel(),
-                                                _stream_ptr(stream, codes.device)))
-    return bits, vals
+    return _debug_widen(_lib.load().xqa_debug_widen_e5m2, codes, stream)
+
+
+def debug_widen_e4m3(codes: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
+    """Widen uint8 E4M3 codes on the GPU with the kernels' own routine."""
+    return _debug_widen(_lib.load().xqa_debug_widen_e4m3, codes, stream)

@@ -90,7 +90,9 @@ xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_page
   a.max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
   a.per_head = h->per_head;
   a.item_stride = h->item_stride;
-  a.scale_log2e = scale * 1.4426950408889634f;
+  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.v_scale = 1.0f;
+  a.kv_format = xqa::kKvE5M2;
   return a;
 }
 
@@ -247,14 +249,31 @@ xqa_status_t xqa_decode_multi(xqa_handle_t h, const void* q, const uint8_t* k_pa
                               const uint8_t* v_pages, const int32_t* block_table,
                               const int32_t* context_lens, int32_t batch, int32_t num_query_tokens,
                               float scale, void* out, void* stream) {
+  return xqa_decode_fp8(h, XQA_KV_E5M2, q, k_pages, v_pages, block_table, context_lens, batch,
+                        num_query_tokens, scale, 1.0f, 1.0f, out, stream);
+}
+
+xqa_status_t xqa_decode_fp8(xqa_handle_t h, xqa_kv_format_t kv_format, const void* q,
+                            const uint8_t* k_pages, const uint8_t* v_pages,
+                            const int32_t* block_table, const int32_t* context_lens, int32_t batch,
+                            int32_t num_query_tokens, float scale, float k_scale, float v_scale,
+                            void* out, void* stream) {
   xqa_status_t st =
       check_decode_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
   if (st != XQA_OK) return st;
+  if (kv_format != XQA_KV_E5M2 && kv_format != XQA_KV_E4M3)
+    return fail(XQA_ERR_INVALID_ARG, "kv_format must be XQA_KV_E5M2 or XQA_KV_E4M3");
   if (num_query_tokens < 1 || num_query_tokens > h->cfg.max_query_tokens)
     return fail(XQA_ERR_INVALID_ARG, "num_query_tokens outside [1, max_query_tokens]");
+  const double score_scale = (double)scale * (double)k_scale * 1.4426950408889634;
+  if (!isfinite(k_scale) || !isfinite(v_scale) || !isfinite((float)score_scale))
+    return fail(XQA_ERR_INVALID_ARG, "k_scale, v_scale and scale * k_scale must be finite");
   if ((st = check_device(h)) != XQA_OK) return st;
-  const xqa::AttendArgs a = attend_args(h, q, k_pages, v_pages, block_table, context_lens, batch,
-                                        scale, out, num_query_tokens);
+  xqa::AttendArgs a = attend_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale,
+                                  out, num_query_tokens);
+  a.scale_log2e = (float)score_scale;
+  a.v_scale = v_scale;
+  a.kv_format = kv_format == XQA_KV_E4M3 ? xqa::kKvE4M3 : xqa::kKvE5M2;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = xqa::launch_split(a, h->grid, s);
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
@@ -315,7 +334,21 @@ xqa_status_t xqa_debug_widen_e5m2(const uint8_t* in, uint16_t* out_f16, float* o
   if ((out_f16 && !aligned(out_f16, 2)) || (out_f32 && !aligned(out_f32, 4)))
     return fail(XQA_ERR_INVALID_ARG, "misaligned output");
   if (n == 0) return XQA_OK;
-  hipError_t e = xqa::launch_widen(in, out_f16, out_f32, n, static_cast<hipStream_t>(stream));
+  hipError_t e =
+      xqa::launch_widen(in, out_f16, out_f32, n, xqa::kKvE5M2, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "widen kernel launch");
+  return XQA_OK;
+}
+
+xqa_status_t xqa_debug_widen_e4m3(const uint8_t* in, uint16_t* out_f16, float* out_f32, int64_t n,
+                                  void* stream) {
+  if (!in || (!out_f16 && !out_f32)) return fail(XQA_ERR_INVALID_ARG, "null pointer");
+  if (n < 0) return fail(XQA_ERR_INVALID_ARG, "negative count");
+  if ((out_f16 && !aligned(out_f16, 2)) || (out_f32 && !aligned(out_f32, 4)))
+    return fail(XQA_ERR_INVALID_ARG, "misaligned output");
+  if (n == 0) return XQA_OK;
+  hipError_t e =
+      xqa::launch_widen(in, out_f16, out_f32, n, xqa::kKvE4M3, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "widen kernel launch");
   return XQA_OK;
 }

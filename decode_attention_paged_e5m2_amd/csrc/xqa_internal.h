@@ -63,6 +63,9 @@ __host__ __device__ inline int32_t item_of_block(int64_t x, int64_t nb_total, in
   return (int32_t)(((x + 1) * items + nb_total - 1) / nb_total - 1);
 }
 
+// Format of the cached K/V bytes.
+enum KvFormat : int32_t { kKvE5M2 = 0, kKvE4M3 = 1 };
+
 struct AttendArgs {
   const uint16_t* q;
   const uint8_t* k_pages;
@@ -80,7 +83,9 @@ struct AttendArgs {
   int32_t max_tokens;
   int32_t per_head;       // grid / Hkv
   int32_t item_stride;    // floats per partial record
-  float scale_log2e;      // scale * log2(e): scores are kept in base-2 units
+  float scale_log2e;      // scale * k_scale * log2(e): scores are kept in base-2 units
+  float v_scale;          // per-tensor V dequantisation scale, applied to the normalised rows
+  int32_t kv_format;      // KvFormat
 };
 
 // KV append: each sequence's new token (binary16 K and V rows for every KV
@@ -102,7 +107,7 @@ hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream);
 hipError_t launch_combine(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_widen(const uint8_t* in, uint16_t* out_f16, float* out_f32, int64_t n,
-                        hipStream_t stream);
+                        int32_t kv_format, hipStream_t stream);
 hipError_t attend_blocks_per_cu(int* blocks);
 
 }  // namespace xqa

@@ -77,17 +77,46 @@ __device__ __forceinline__ uint32_t widen_hi(uint32_t x) {   // codes 2, 3 of x
   return __builtin_amdgcn_perm(0u, x, 0x030C020Cu);
 }
 
+// E4M3 (OCP, bias 7): two codes of x -> two binary16 values with the gfx950
+// conversion instruction at scale 1. Every E4M3 value is a binary16 value,
+// so this is exact (checked for all 256 codes through xqa_debug_widen_e4m3).
+__device__ __forceinline__ uint32_t e4m3_lo(uint32_t x) {   // codes 0, 1 of x
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t e4m3_hi(uint32_t x) {   // codes 2, 3 of x
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true));
+}
+
+template <int F>
+__device__ __forceinline__ uint32_t widen_k_lo(uint32_t x) {
+  return F == kKvE4M3 ? e4m3_lo(x) : widen_lo(x);
+}
+template <int F>
+__device__ __forceinline__ uint32_t widen_k_hi(uint32_t x) {
+  return F == kKvE4M3 ? e4m3_hi(x) : widen_hi(x);
+}
+
 // 4x4 byte transpose across a lane quad plus widening. Lane i of the quad
 // holds x = row i (4 consecutive head-dim codes of token i); on return it
 // holds column i as binary16 pairs: h0 = (row0, row1), h1 = (row2, row3).
 // Stage 1 swaps 16-bit halves with lane i^2, stage 2 bytes with lane i^1.
+// E5M2: the last two v_perm_b32 also widen (selh0, selh1). E4M3: one v_perm
+// puts the column's bytes in row order (selector in selh0) and the
+// conversion instruction widens them.
+template <int F>
 __device__ __forceinline__ void transpose_widen(uint32_t x, uint32_t sel1, uint32_t selh0,
                                                 uint32_t selh1, uint32_t& h0, uint32_t& h1) {
   const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
   const uint32_t t = __builtin_amdgcn_perm(y, x, sel1);
   const uint32_t z = (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
-  h0 = __builtin_amdgcn_perm(z, t, selh0);
-  h1 = __builtin_amdgcn_perm(z, t, selh1);
+  if constexpr (F == kKvE4M3) {
+    const uint32_t c = __builtin_amdgcn_perm(z, t, selh0);
+    h0 = e4m3_lo(c);
+    h1 = e4m3_hi(c);
+  } else {
+    h0 = __builtin_amdgcn_perm(z, t, selh0);
+    h1 = __builtin_amdgcn_perm(z, t, selh1);
+  }
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -258,7 +287,7 @@ __device__ __forceinline__ void load_block(RawBlock& r, const uint8_t* ka, const
 // t_end: end of the segment's tokens (V rows past it are zeroed). row_end:
 // this lane's query row sees tokens < row_end (<= t_end; smaller for the
 // earlier of several query tokens). t_mask: the smallest row_end of the wave.
-template <bool kTail>
+template <bool kTail, int F>
 __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4], WaveState& st,
                                               float scale_log2e, int tok0, int t_end, int row_end,
                                               int t_mask, int lane, uint32_t sel1, uint32_t selh0,
@@ -288,8 +317,8 @@ __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4],
     const u32x4 kb = r.k[2 + (i >> 1)];
     const uint32_t a0 = ka[(i & 1) * 2], a1 = ka[(i & 1) * 2 + 1];
     const uint32_t b0 = kb[(i & 1) * 2], b1 = kb[(i & 1) * 2 + 1];
-    const u32x4 fa = {widen_lo(a0), widen_hi(a0), widen_lo(a1), widen_hi(a1)};
-    const u32x4 fb = {widen_lo(b0), widen_hi(b0), widen_lo(b1), widen_hi(b1)};
+    const u32x4 fa = {widen_k_lo<F>(a0), widen_k_hi<F>(a0), widen_k_lo<F>(a1), widen_k_hi<F>(a1)};
+    const u32x4 fb = {widen_k_lo<F>(b0), widen_k_hi<F>(b0), widen_k_lo<F>(b1), widen_k_hi<F>(b1)};
     sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, fa), qf[i], sa, 0, 0, 0);
     sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, fb), qf[i], sb, 0, 0, 0);
   }
@@ -370,8 +399,8 @@ __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4],
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t a0, a1, b0, b1;
-      transpose_widen(r.v[L][k], sel1, selh0, selh1, a0, a1);
-      transpose_widen(r.v[2 + L][k], sel1, selh0, selh1, b0, b1);
+      transpose_widen<F>(r.v[L][k], sel1, selh0, selh1, a0, a1);
+      transpose_widen<F>(r.v[2 + L][k], sel1, selh0, selh1, b0, b1);
       const u32x4 vf = {a0, a1, b0, b1};
       st.o[L * 4 + k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, vf), pfrag,
                                                              st.o[L * 4 + k], 0, 0, 0);
@@ -397,6 +426,7 @@ struct SplitShared {
 // min(n, 32 jb_hi)) for KV head h. The four waves take interleaved blocks,
 // then merge in LDS. `direct`: the segment is the whole sequence, so the
 // normalised output is written; otherwise the state goes to `rec`.
+template <int F>
 __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh, int b, int h,
                                             int n, int jb_lo, int jb_hi, bool direct, float* rec,
                                             int lane, int wave) {
@@ -430,7 +460,9 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
   const int koff = g * kHeadDim + 16 * q;
   const int voff = (4 * q + (lane & 3)) * kHeadDim + 16 * ((lane >> 2) & 3);
   const uint32_t sel1 = (lane & 2) ? 0x03020706u : 0x05040100u;
-  const uint32_t selh0 = (lane & 1) ? 0x010C050Cu : 0x040C000Cu;
+  // E4M3 uses selh0 for the row-order byte selector of the transpose.
+  const uint32_t selh0 = F == kKvE4M3 ? ((lane & 1) ? 0x03070105u : 0x06020400u)
+                                      : ((lane & 1) ? 0x010C050Cu : 0x040C000Cu);
   const uint32_t selh1 = (lane & 1) ? 0x030C070Cu : 0x060C020Cu;
 
   WaveState st;
@@ -473,20 +505,20 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
     int mm = 0;
     for (; mm + 2 < cnt; mm += 2) {
       issue(B, mm + 1);
-      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
+      process_block<false, F>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
                            selh0, selh1);
       issue(A, mm + 2);
-      process_block<false>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, row_end, t_mask, lane,
+      process_block<false, F>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, row_end, t_mask, lane,
                            sel1, selh0, selh1);
     }
     if (cnt - mm == 2) {
       issue(B, mm + 1);
-      process_block<false>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
+      process_block<false, F>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
                            selh0, selh1);
-      process_block<true>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, row_end, t_mask, lane,
+      process_block<true, F>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, row_end, t_mask, lane,
                           sel1, selh0, selh1);
     } else {
-      process_block<true>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
+      process_block<true, F>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
                           selh0, selh1);
     }
   }
@@ -524,7 +556,7 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
       o += f * *(const float4v*)&sh.o[w][gg][d4];
     }
     if (direct) {
-      const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;   // a row with no visible token is zero
+      const float inv = Ls > 0.f ? a.v_scale / Ls : 0.f;   // a row with no visible token is zero
       uint2 packed;
       packed.x = pack_half2(o[0] * inv, o[1] * inv);
       packed.y = pack_half2(o[2] * inv, o[3] * inv);
@@ -540,6 +572,7 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
   __syncthreads();   // the LDS state is reused by the next segment
 }
 
+template <int F>
 __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
   __shared__ SplitShared sh;
   const int lane = threadIdx.x & 63;
@@ -563,8 +596,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
     const long long seg_hi = hi < sq.off + nb ? hi : sq.off + nb;
     const bool direct = item_of_block(sq.off, NB, P) == item_of_block(sq.off + nb - 1, NB, P);
     float* rec = a.partials + ((long long)(2 * item + (first ? 0 : 1)) * Hkv + h) * a.item_stride;
-    run_segment(a, sh, sq.b, h, sq.n, (int)(seg_lo - sq.off), (int)(seg_hi - sq.off), direct, rec,
-                lane, wave);
+    run_segment<F>(a, sh, sq.b, h, sq.n, (int)(seg_lo - sq.off), (int)(seg_hi - sq.off), direct,
+                   rec, lane, wave);
     if (sq.off + nb >= hi) break;
     first = false;
     do {   // next non-empty sequence (one exists: this item has blocks left)
@@ -650,7 +683,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) 
         o1 += w * ov[k].y;
       }
     }
-    const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;   // a row with no visible token is zero
+    const float inv = Ls > 0.f ? a.v_scale / Ls : 0.f;   // a row with no visible token is zero
     *(uint32_t*)(out_row(a, b, h, gg) + c) = pack_half2(o0 * inv, o1 * inv);
   }
 }
@@ -704,6 +737,7 @@ __global__ void append_kernel(AppendArgs a) {
 // ------------------------------------------------------------ widen (test)
 // Each thread widens one group of four codes with the same helpers the K
 // path uses, so every byte position of both selectors is exercised.
+template <int F>
 __global__ void widen_kernel(const uint8_t* in, uint16_t* out16, float* out32, long long n) {
   const long long grp = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long i0 = grp * 4;
@@ -712,7 +746,7 @@ __global__ void widen_kernel(const uint8_t* in, uint16_t* out16, float* out32, l
   for (int k = 0; k < 4; ++k) {
     if (i0 + k < n) x |= (uint32_t)in[i0 + k] << (8 * k);
   }
-  const uint32_t lo = widen_lo(x), hi = widen_hi(x);
+  const uint32_t lo = widen_k_lo<F>(x), hi = widen_k_hi<F>(x);
   const uint16_t bits[4] = {(uint16_t)(lo & 0xFFFFu), (uint16_t)(lo >> 16), (uint16_t)(hi & 0xFFFFu),
                             (uint16_t)(hi >> 16)};
   for (int k = 0; k < 4; ++k) {
@@ -725,7 +759,11 @@ __global__ void widen_kernel(const uint8_t* in, uint16_t* out16, float* out32, l
 }  // namespace
 
 hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(split_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  if (a.kv_format == kKvE4M3) {
+    hipLaunchKernelGGL(split_kernel<kKvE4M3>, dim3(grid), dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(split_kernel<kKvE5M2>, dim3(grid), dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -744,17 +782,29 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_widen(const uint8_t* in, uint16_t* out_f16, float* out_f32, int64_t n,
-                        hipStream_t stream) {
+                        int32_t kv_format, hipStream_t stream) {
   const long long groups = (n + 3) / 4;
   const int threads = 256;
   const long long blocks = (groups + threads - 1) / threads;
-  hipLaunchKernelGGL(widen_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, in, out_f16,
-                     out_f32, (long long)n);
+  if (kv_format == kKvE4M3) {
+    hipLaunchKernelGGL(widen_kernel<kKvE4M3>, dim3((unsigned)blocks), dim3(threads), 0, stream, in,
+                       out_f16, out_f32, (long long)n);
+  } else {
+    hipLaunchKernelGGL(widen_kernel<kKvE5M2>, dim3((unsigned)blocks), dim3(threads), 0, stream, in,
+                       out_f16, out_f32, (long long)n);
+  }
   return hipGetLastError();
 }
 
+// Resident split workgroups per CU: the smaller of the two formats' figures,
+// so one grid serves both.
 hipError_t attend_blocks_per_cu(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, split_kernel, kThreads, 0);
+  int a = 0, b = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, split_kernel<kKvE5M2>, kThreads, 0);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, split_kernel<kKvE4M3>, kThreads, 0);
+  *blocks = a < b ? a : b;
+  return e;
 }
 
 }  // namespace xqa

@@ -60,6 +60,12 @@ typedef enum {
   XQA_ERR_HIP = 4            /* HIP runtime error (no device, launch failure, ...)    */
 } xqa_status_t;
 
+/* Format of the cached K/V bytes (xqa_decode_fp8). */
+typedef enum {
+  XQA_KV_E5M2 = 0,           /* OCP FP8 E5M2: the code is the high byte of binary16      */
+  XQA_KV_E4M3 = 1            /* OCP FP8 E4M3 ("E4M3FN"): bias 7, max 448, no infinities  */
+} xqa_kv_format_t;
+
 typedef struct {
   int32_t max_batch;         /* >= 1: largest batch a decode call may pass              */
   int32_t num_q_heads;       /* Hq, multiple of num_kv_heads                            */
@@ -131,6 +137,24 @@ xqa_status_t xqa_decode_multi(xqa_handle_t handle, const void* q, const uint8_t*
                               const int32_t* context_lens, int32_t batch, int32_t num_query_tokens,
                               float scale, void* out, void* stream);
 
+/* The general form: an E5M2 or E4M3 cache with per-tensor dequantisation
+ * scales, one or several query tokens. Cached values are k_scale * dec(code)
+ * and v_scale * dec(code), dec() the format's exact decode (E4M3 widens to
+ * binary16 exactly with the gfx950 conversion instruction). Scores are
+ * scale * k_scale * q.k (the product formed in double and rounded once to
+ * fp32); outputs are v_scale times the normalised sum. The E4M3 reading
+ * follows the page "[Kernel][WIP] Follow up FlashNext batch HC fusion and
+ * QSA route audit" (section Test Result), which names E4M3 as a cache format
+ * still awaiting quality admission. xqa_decode_multi is kv_format
+ * XQA_KV_E5M2 with both scales 1. Errors: as for xqa_decode_multi;
+ * INVALID_ARG also for an unknown kv_format or a non-finite k_scale,
+ * v_scale or scale * k_scale. */
+xqa_status_t xqa_decode_fp8(xqa_handle_t handle, xqa_kv_format_t kv_format, const void* q,
+                            const uint8_t* k_pages, const uint8_t* v_pages,
+                            const int32_t* block_table, const int32_t* context_lens, int32_t batch,
+                            int32_t num_query_tokens, float scale, float k_scale, float v_scale,
+                            void* out, void* stream);
+
 /* First stage of xqa_decode alone (device-side plan, page gather, widening,
  * QK, online softmax, PV): rows of sequences that fit one work item are
  * written to out; the others leave split states in the workspace. Same
@@ -184,6 +208,11 @@ xqa_status_t xqa_plan(xqa_handle_t handle, const int32_t* context_lens_host, int
  * kernel uses for K. out_f16 receives the binary16 bit patterns, out_f32 the
  * same values as fp32 (either output may be NULL). Device pointers. */
 xqa_status_t xqa_debug_widen_e5m2(const uint8_t* in, uint16_t* out_f16, float* out_f32,
+                                  int64_t n, void* stream);
+
+/* Test hook: the same for E4M3 codes and the device routine the split
+ * kernel uses for E4M3 K. */
+xqa_status_t xqa_debug_widen_e4m3(const uint8_t* in, uint16_t* out_f16, float* out_f32,
                                   int64_t n, void* stream);
 
 /* Static name of a status code. */

@@ -92,3 +92,24 @@ def test_fast_and_f64_agree_large_parallel_path():
     x[: 1 << 20] *= np.float32(1e-4)
     x[1 << 20: 1 << 21] *= np.float32(2e4)
     assert (quantize_e5m2(x) == quantize_e5m2_f64(x)).all()
+
+
+def test_e4m3_input_quantizer_is_nearest_even_saturating():
+    # The E4M3 input generator against a brute-force nearest search over every
+    # finite E4M3 value (ties to the even code, saturation at +-448).
+    from oracle.e4m3 import E4M3_TABLE
+    from workloads.quantize import quantize_e4m3
+    rng = np.random.default_rng(17)
+    x = np.concatenate([
+        rng.standard_normal(20000) * np.exp(rng.uniform(-12, 7, 20000)),
+        [0.0, -0.0, 448.0, 464.0, 1e6, -1e6, 2.0 ** -10, 3 * 2.0 ** -10, 1.0625, 1.1875],
+    ]).astype(np.float32)
+    got = quantize_e4m3(x).astype(np.int64)
+    fin = np.array([c for c in range(256) if np.isfinite(E4M3_TABLE[c])])
+    for xi, gi in zip(x.astype(np.float64), got):
+        same_sign = fin[(fin >= 128) == bool(np.signbit(xi))]
+        d = np.abs(E4M3_TABLE[same_sign] - xi)
+        best = same_sign[d == d.min()]
+        assert gi in best, (xi, gi, best)
+        if best.size > 1:
+            assert gi % 2 == 0, (xi, gi, best)

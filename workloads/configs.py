@@ -27,7 +27,7 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from .quantize import quantize_e5m2, POISON_CODE
+from .quantize import quantize_e4m3, quantize_e5m2, POISON_CODE
 
 HEAD_DIM = 128
 PAGE_SIZE = 16
@@ -63,6 +63,7 @@ class Workload:
     k_tokens: List[np.ndarray] = field(repr=False)   # uint8 [n_b, Hkv, D] per sequence
     v_tokens: List[np.ndarray] = field(repr=False)
     scale: float = DEFAULT_SCALE
+    kv_format: str = "e5m2"     # byte format of k_tokens / v_tokens: "e5m2" or "e4m3"
 
     @property
     def group(self) -> int:
@@ -106,8 +107,9 @@ def make_custom(context_lens: Sequence[int], num_kv_heads: int, num_q_heads: int
                 outlier_scale: float = 1000.0, scale: float = DEFAULT_SCALE,
                 name: str = "custom", rng: Optional[np.random.Generator] = None,
                 head_dim: int = HEAD_DIM, page_size: int = PAGE_SIZE,
-                with_tokens: bool = True) -> Workload:
+                with_tokens: bool = True, kv_format: str = "e5m2") -> Workload:
     """Build a workload with the recipe above for arbitrary context lengths."""
+    quantize = {"e5m2": quantize_e5m2, "e4m3": quantize_e4m3}[kv_format]
     if rng is None:
         rng = np.random.default_rng(seed)
     ctx = np.asarray(context_lens, dtype=np.int64)
@@ -152,8 +154,8 @@ def make_custom(context_lens: Sequence[int], num_kv_heads: int, num_q_heads: int
             mv = rng.random((n, num_kv_heads, head_dim)) < outlier_frac
             kf[mk] *= np.float32(outlier_scale)
             vf[mv] *= np.float32(outlier_scale)
-        k_tokens.append(quantize_e5m2(kf))
-        v_tokens.append(quantize_e5m2(vf))
+        k_tokens.append(quantize(kf))
+        v_tokens.append(quantize(vf))
 
     return Workload(
         name=name, seed=tuple(np.atleast_1d(seed).tolist()) if seed is not None else (),
@@ -161,10 +163,11 @@ def make_custom(context_lens: Sequence[int], num_kv_heads: int, num_q_heads: int
         head_dim=head_dim, page_size=P, max_pages_per_seq=int(max_pages_per_seq),
         num_pages=num_pages, poison_page=poison,
         context_lens=ctx.astype(np.int32), block_table=block_table, q=q,
-        k_tokens=k_tokens, v_tokens=v_tokens, scale=float(np.float32(scale)))
+        k_tokens=k_tokens, v_tokens=v_tokens, scale=float(np.float32(scale)), kv_format=kv_format)
 
 
-def make_config(index: int, variant: int = 0, with_tokens: bool = True) -> Workload:
+def make_config(index: int, variant: int = 0, with_tokens: bool = True,
+                kv_format: str = "e5m2") -> Workload:
     """Config 1..5 (see module docstring), deterministic in (index, variant).
 
     ``with_tokens=False`` stops after the block table and q (same draws), for
@@ -173,7 +176,7 @@ def make_config(index: int, variant: int = 0, with_tokens: bool = True) -> Workl
     seed = [1000 + index, variant]
     rng = np.random.default_rng(seed)
     name = f"cfg{index}_{CONFIG_NAMES[index]}_v{variant}"
-    kw = dict(name=name, rng=rng, with_tokens=with_tokens)
+    kw = dict(name=name, rng=rng, with_tokens=with_tokens, kv_format=kv_format)
     if index == 1:
         return make_custom([256], 1, 8, seed, pool_pages=16, max_pages_per_seq=16,
                            identity_pages=True, **kw)

@@ -94,3 +94,19 @@ def quantize_e5m2_f64(x) -> np.ndarray:
         code[nrm] = ((e + 15) << 2) + (qq - 4)
     code = code | (neg.astype(np.int64) << 7)
     return code.astype(np.uint8)
+
+
+E4M3_MAX_FINITE = 448.0
+
+
+def quantize_e4m3(x) -> np.ndarray:
+    """float -> OCP E4M3 codes (uint8): round to nearest even, saturating at +-448.
+
+    Input generation only (the kernels decode E4M3; they never encode it):
+    values are clipped to the largest finite magnitude and converted by
+    torch's float8_e4m3fn cast, which rounds to nearest even.
+    """
+    import torch
+    a = np.clip(np.asarray(x, dtype=np.float32), -E4M3_MAX_FINITE, E4M3_MAX_FINITE)
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
