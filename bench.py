@@ -42,8 +42,8 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE x2.00, WRITE_SIZE x1.00). Valid only for the kernel sources
 # whose hash is recorded; any change to them reports null until re-measured.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "e8325f8f680cf64bb7c006fef3c3d5c1ac6011db7bfa02414df0d434496f237c",
-    "fetch_kib": 133314.7, "fetch_scale": 2.0,
+    "sources_sha256": "d6e351adf31899e96c134d1baa80d0a0fbb9ab6dc0f024720037230474b10ad2",
+    "fetch_kib": 133328.5, "fetch_scale": 2.0,
     "write_kib": 2323.8, "write_scale": 1.0,
 }
 
@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=0, help="oracle repetitions (0 = auto, ~10-20 s)")
     ap.add_argument("--quick", action="store_true", help="skip A/B/B/A and warm-mode extras")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the multi-token, E4M3 and KV-append legs (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (5x), the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counter readings")
@@ -326,7 +328,7 @@ def main():
     # heads of a KV head times two tokens fill the 16-row matrix-core tile
     # that one token leaves half empty at G = 8; the KV bytes are the same.
     G = w0.num_q_heads // w0.num_kv_heads
-    if 2 * G <= 16:
+    if 2 * G <= 16 and not args.no_extras:
         gen2 = torch.Generator().manual_seed(11)
         xqa2 = Xqa(max_batch=w0.batch, num_q_heads=w0.num_q_heads, num_kv_heads=w0.num_kv_heads,
                    max_pages_per_seq=w0.max_pages_per_seq, max_query_tokens=2)
@@ -359,87 +361,88 @@ def main():
         log(f"two query tokens per sequence: {us_m2:.2f} us/step ({us_m2 / us_step:.3f}x one token)")
         xqa2.close()
 
-    # ------------------------------------------------------------ E4M3 cache
-    # The same workload with its K/V quantised to E4M3 and per-tensor scales
-    # (xqa_decode_fp8): same bytes per step, a different widening.
-    works4 = [make_config(args.config, v, kv_format="e4m3") for v in range(R)]
-    devs4 = [to_device(w, dev) for w in works4]
-    out4 = [torch.empty_like(d.q) for d in devs4]
+    if not args.no_extras:
+        # ------------------------------------------------------------ E4M3 cache
+        # The same workload with its K/V quantised to E4M3 and per-tensor scales
+        # (xqa_decode_fp8): same bytes per step, a different widening.
+        works4 = [make_config(args.config, v, kv_format="e4m3") for v in range(R)]
+        devs4 = [to_device(w, dev) for w in works4]
+        out4 = [torch.empty_like(d.q) for d in devs4]
 
-    def call4(i):
-        d = devs4[i]
-        xqa.decode(q=d.q, k_pages=d.k_pages, v_pages=d.v_pages, block_table=d.block_table,
-                   context_lens=d.context_lens, scale=w0.scale, out=out4[i], kv_format="e4m3",
-                   k_scale=0.5, v_scale=2.0)
+        def call4(i):
+            d = devs4[i]
+            xqa.decode(q=d.q, k_pages=d.k_pages, v_pages=d.v_pages, block_table=d.block_table,
+                       context_lens=d.context_lens, scale=w0.scale, out=out4[i], kv_format="e4m3",
+                       k_scale=0.5, v_scale=2.0)
 
-    for i in range(R):
-        call4(i)
-    torch.cuda.synchronize()
-    graph4 = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph4):
         for i in range(R):
             call4(i)
-    for _ in range(max(args.warmup // R, 2)):
-        graph4.replay()
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    for _ in range(steps // R):
-        graph4.replay()
-    torch.cuda.synchronize()
-    us_e4 = (time.perf_counter() - t) / steps * 1e6
-    bytes4 = statistics.mean(w.kv_bytes for w in works4)
-    detail["e4m3_scaled"] = {"us_per_step_graph_Rstep": us_e4, "kv_gbs": bytes4 / us_e4 / 1e3,
-                             "ratio_to_e5m2": us_e4 / us_step}
-    log(f"E4M3 cache with scales: {us_e4:.2f} us/step ({us_e4 / us_step:.3f}x E5M2)")
-    del graph4, devs4, out4, works4
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        graph4 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph4):
+            for i in range(R):
+                call4(i)
+        for _ in range(max(args.warmup // R, 2)):
+            graph4.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps // R):
+            graph4.replay()
+        torch.cuda.synchronize()
+        us_e4 = (time.perf_counter() - t) / steps * 1e6
+        bytes4 = statistics.mean(w.kv_bytes for w in works4)
+        detail["e4m3_scaled"] = {"us_per_step_graph_Rstep": us_e4, "kv_gbs": bytes4 / us_e4 / 1e3,
+                                 "ratio_to_e5m2": us_e4 / us_step}
+        log(f"E4M3 cache with scales: {us_e4:.2f} us/step ({us_e4 / us_step:.3f}x E5M2)")
+        del graph4, devs4, out4, works4
+        torch.cuda.synchronize()
 
-    # ------------------------------------------------------------ KV append
-    # The step before decode in serving: each sequence's new token written
-    # into its page slot as E5M2 (xqa_append_kv). Timed per launch with HIP
-    # events on the launch stream, and inside one graph holding append +
-    # decode for each of the R steps. It rewrites token n - 1 of every
-    # sequence, so it runs after every decode measurement above.
-    gen = torch.Generator().manual_seed(7)
-    k_new = [torch.randn((w.batch, w.num_kv_heads, w.head_dim), generator=gen).half().to(dev)
-             for w in works]
-    v_new = [torch.randn((w.batch, w.num_kv_heads, w.head_dim), generator=gen).half().to(dev)
-             for w in works]
+        # ------------------------------------------------------------ KV append
+        # The step before decode in serving: each sequence's new token written
+        # into its page slot as E5M2 (xqa_append_kv). Timed per launch with HIP
+        # events on the launch stream, and inside one graph holding append +
+        # decode for each of the R steps. It rewrites token n - 1 of every
+        # sequence, so it runs after every decode measurement above.
+        gen = torch.Generator().manual_seed(7)
+        k_new = [torch.randn((w.batch, w.num_kv_heads, w.head_dim), generator=gen).half().to(dev)
+                 for w in works]
+        v_new = [torch.randn((w.batch, w.num_kv_heads, w.head_dim), generator=gen).half().to(dev)
+                 for w in works]
 
-    def append(i):
-        d = devs[i]
-        xqa.append_kv(k_new=k_new[i], v_new=v_new[i], block_table=d.block_table,
-                      context_lens=d.context_lens, k_pages=d.k_pages, v_pages=d.v_pages)
+        def append(i):
+            d = devs[i]
+            xqa.append_kv(k_new=k_new[i], v_new=v_new[i], block_table=d.block_table,
+                          context_lens=d.context_lens, k_pages=d.k_pages, v_pages=d.v_pages)
 
-    for i in range(R):
-        append(i)
-    torch.cuda.synchronize()
-    ev_a = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(n_ev)]
-    for k in range(n_ev):
-        ev_a[k][0].record(stream)
-        append(k % R)
-        ev_a[k][1].record(stream)
-    torch.cuda.synchronize()
-    append_us = statistics.mean(ev_a[k][0].elapsed_time(ev_a[k][1]) for k in range(n_ev)) * 1e3
-    full = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(full):
         for i in range(R):
             append(i)
-            call(devs[i], outs[i])
-    for _ in range(max(args.warmup // R, 2)):
-        full.replay()
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    for _ in range(steps // R):
-        full.replay()
-    torch.cuda.synchronize()
-    us_full = (time.perf_counter() - t) / steps * 1e6
-    detail["append_kv"] = {
-        "us_per_launch_mean": append_us,
-        "bytes_per_launch": w0.batch * w0.num_kv_heads * w0.head_dim * 2 * (2 + 1),
-        "us_per_step_graph_Rstep_append_plus_decode": us_full,
-    }
-    log(f"KV append: {append_us:.2f} us per launch; append + decode graph {us_full:.2f} us/step")
+        torch.cuda.synchronize()
+        ev_a = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(n_ev)]
+        for k in range(n_ev):
+            ev_a[k][0].record(stream)
+            append(k % R)
+            ev_a[k][1].record(stream)
+        torch.cuda.synchronize()
+        append_us = statistics.mean(ev_a[k][0].elapsed_time(ev_a[k][1]) for k in range(n_ev)) * 1e3
+        full = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(full):
+            for i in range(R):
+                append(i)
+                call(devs[i], outs[i])
+        for _ in range(max(args.warmup // R, 2)):
+            full.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps // R):
+            full.replay()
+        torch.cuda.synchronize()
+        us_full = (time.perf_counter() - t) / steps * 1e6
+        detail["append_kv"] = {
+            "us_per_launch_mean": append_us,
+            "bytes_per_launch": w0.batch * w0.num_kv_heads * w0.head_dim * 2 * (2 + 1),
+            "us_per_step_graph_Rstep_append_plus_decode": us_full,
+        }
+        log(f"KV append: {append_us:.2f} us per launch; append + decode graph {us_full:.2f} us/step")
 
     line = {
         "metric": METRIC,
