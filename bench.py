@@ -42,19 +42,25 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE x2.00, WRITE_SIZE x1.00). Valid only for the kernel sources
 # whose hash is recorded; any change to them reports null until re-measured.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "d6e351adf31899e96c134d1baa80d0a0fbb9ab6dc0f024720037230474b10ad2",
+    "sources_sha256": "1c93fb6f795fbc373f3ffe407675c5d1e664eda083942cf5facc6fb6cb6b1513",
     "fetch_kib": 133328.5, "fetch_scale": 2.0,
     "write_kib": 2323.8, "write_scale": 1.0,
 }
 
 
 def kernel_sources_sha256():
+    """sha256 of the kernel sources' code: comments and blank lines removed,
+    so that only a change to the code itself invalidates measured counters."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_paged_e5m2_amd", "csrc")
     for f in ("xqa_kernels.hip", "xqa_internal.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
     return h.hexdigest()
 
 

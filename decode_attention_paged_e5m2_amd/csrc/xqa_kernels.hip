@@ -1,9 +1,11 @@
-// Paged FP8-E5M2 grouped-query decode attention: gfx950 kernels.
+// Paged FP8 grouped-query decode attention: gfx950 kernels.
 //
 // What is computed follows the page "[Kernel][SM70] Pipeline batched E5M2
 // XQA decode" (Purpose; Pending work and gates): one query token per
 // sequence attends over its paged E5M2 K/V cache, query heads sharing KV
-// heads. The phases that page lists -- K load + E5M2 conversion, QK, V load
+// heads. The same kernels also take several new query tokens per sequence
+// (causal among themselves), an E4M3 cache with per-tensor K/V scales, and
+// a small kernel writes each step's new token into the cache. The phases that page lists -- K load + E5M2 conversion, QK, V load
 // + conversion, PV, synchronisation -- map onto the code below; the tiling
 // is designed for CDNA4 (64-wide waves, MFMA, DPP) rather than taken from it.
 //
@@ -20,17 +22,21 @@
 //   K: lane l reads token l%16 of the page, head-dim bytes
 //      [16q, 16q+16) and [64+16q, 64+16q+16) (q = l/16): each load
 //      instruction covers 64 contiguous bytes of all 16 token rows.
-//      Widening is one v_perm_b32 per two codes (the E5M2 code is the high
-//      byte of its binary16 value).
+//      Widening is one instruction per two codes: v_perm_b32 for E5M2 (the
+//      code is the high byte of its binary16 value), the conversion
+//      instruction for E4M3 (every E4M3 value is a binary16 value).
 //   QK: S^T = K . Q^T with v_mfma_f32_16x16x32_f16, M = the 16 tokens of a
-//      page, N = the query heads of the group (padded to 16), four MFMAs
-//      over head_dim 128. The contraction index may be permuted freely as
+//      page, N = the query rows (the G heads of the group times the M query
+//      tokens, padded to 16), four MFMAs over head_dim 128. The contraction index may be permuted freely as
 //      long as the K and Q fragments agree, which is what lets K go straight
 //      from its load layout into the A operand.
-//   Softmax: the accumulator gives lane l the scores of head l%16 for
+//   Softmax: the accumulator gives lane l the scores of query row l%16 for
 //      tokens 4q..4q+3; the block max over a 32-token block is a register
-//      max plus two lane-xor steps (16, 32). Scores are kept in base-2 units
-//      (scale * log2 e folded in) and exponentiated with v_exp_f32.
+//      max plus two lane-swap steps (16, 32). Scores are kept in base-2
+//      units (scale * k_scale * log2 e folded in) and exponentiated with
+//      v_exp_f32 against a reference maximum that is raised only when a
+//      block passes it by more than 2^8. Tail blocks mask tokens past the
+//      segment and, per row, past the row's query position.
 //   PV: O^T = V^T . P^T with v_mfma_f32_16x16x32_f16 over the 32 tokens of
 //      the block. P^T needs no data movement: the QK accumulator is already
 //      the B-operand layout once converted to binary16. V^T does: V's
@@ -45,8 +51,8 @@
 //
 // The combine kernel then merges the states of every split sequence with
 // the exact log-sum-exp rule M = max m_s, L = sum l_s 2^(m_s-M),
-// out = sum 2^(m_s-M) O_s / L (split order, in rounds of kCombineRound
-// states), and writes the zero rows of empty sequences.
+// out = v_scale * sum 2^(m_s-M) O_s / L (split order, in rounds of
+// kCombineRound states), and writes the zero rows of empty sequences.
 // The kernel boundary makes the split states visible across the chip's
 // separately cached dies without any in-kernel cache write-back.
 //
