@@ -443,12 +443,30 @@ def main():
             full.replay()
         torch.cuda.synchronize()
         us_full = (time.perf_counter() - t) / steps * 1e6
+        # The same step with the append fused into the decode (xqa_decode_append).
+        fused = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(fused):
+            for i in range(R):
+                d = devs[i]
+                xqa.decode_append(q=d.q, k_new=k_new[i], v_new=v_new[i], k_pages=d.k_pages,
+                                  v_pages=d.v_pages, block_table=d.block_table,
+                                  context_lens=d.context_lens, scale=w0.scale, out=outs[i])
+        for _ in range(max(args.warmup // R, 2)):
+            fused.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps // R):
+            fused.replay()
+        torch.cuda.synchronize()
+        us_fused = (time.perf_counter() - t) / steps * 1e6
         detail["append_kv"] = {
             "us_per_launch_mean": append_us,
             "bytes_per_launch": w0.batch * w0.num_kv_heads * w0.head_dim * 2 * (2 + 1),
             "us_per_step_graph_Rstep_append_plus_decode": us_full,
+            "us_per_step_graph_Rstep_fused_append_decode": us_fused,
         }
-        log(f"KV append: {append_us:.2f} us per launch; append + decode graph {us_full:.2f} us/step")
+        log(f"KV append: {append_us:.2f} us per launch; append + decode graph {us_full:.2f} us/step; "
+            f"fused {us_fused:.2f} us/step")
 
     line = {
         "metric": METRIC,

@@ -14,7 +14,7 @@ XQA_ERR_HIP = 4
 
 EXPORTED = [
     "xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_multi",
-    "xqa_decode_fp8", "xqa_decode_split",
+    "xqa_decode_fp8", "xqa_decode_append", "xqa_decode_split",
     "xqa_decode_combine", "xqa_append_kv", "xqa_plan", "xqa_debug_widen_e5m2",
     "xqa_debug_widen_e4m3", "xqa_status_string", "xqa_last_error",
 ]
@@ -76,6 +76,7 @@ def load() -> ctypes.CDLL:
     lib.xqa_decode_split.argtypes = dec
     lib.xqa_decode_combine.argtypes = [vp, vp, i32, vp, vp]
     lib.xqa_append_kv.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.xqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp]
     lib.xqa_plan.argtypes = [vp, ctypes.POINTER(i32), i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.xqa_debug_widen_e5m2.argtypes = [vp, vp, vp, i64, vp]
     lib.xqa_debug_widen_e4m3.argtypes = [vp, vp, vp, i64, vp]
@@ -84,7 +85,7 @@ def load() -> ctypes.CDLL:
     lib.xqa_last_error.argtypes = []
     lib.xqa_last_error.restype = ctypes.c_char_p
     for name in ("xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_multi",
-                 "xqa_decode_fp8", "xqa_debug_widen_e4m3", "xqa_decode_split",
+                 "xqa_decode_fp8", "xqa_debug_widen_e4m3", "xqa_decode_append", "xqa_decode_split",
                  "xqa_decode_combine", "xqa_append_kv", "xqa_plan", "xqa_debug_widen_e5m2"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib

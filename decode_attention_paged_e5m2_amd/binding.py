@@ -208,6 +208,27 @@ class Xqa:
                                              _ptr(context_lens), int(batch), _ptr(k_pages),
                                              _ptr(v_pages), _stream_ptr(stream, dev)))
 
+    def decode_append(self, *, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                      k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                      context_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                      batch: Optional[int] = None,
+                      stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """append_kv + decode in one call (xqa_decode_append): the new token's
+        rows are written into the pages and attended to; q is [B, Hq, D]."""
+        _need(isinstance(q, torch.Tensor) and q.dim() == 3, "decode_append() takes q [B, Hq, D]")
+        out, args = self._args(q, k_pages, v_pages, block_table, context_lens, out, batch, scale, stream)
+        batch = int(args[6])
+        H, D = self.num_kv_heads, self.head_dim
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            _need(isinstance(t, torch.Tensor) and t.dtype == torch.float16 and t.device == self.device
+                  and t.is_contiguous(), f"{name} must be contiguous float16 on {self.device}")
+            _need(t.dim() == 3 and t.shape[0] >= batch and t.shape[1:] == (H, D),
+                  f"{name} must be [>= batch, {H}, {D}]")
+        h, qp, kp, vp, btp, clp, b, sc, op, st = args
+        _lib.check(_lib.load().xqa_decode_append(h, qp, _ptr(k_new), _ptr(v_new), kp, vp, btp, clp,
+                                                 b, sc, op, st))
+        return out
+
     # ----------------------------------------------------------- lifetime
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value is not None:

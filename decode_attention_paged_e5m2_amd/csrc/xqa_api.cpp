@@ -93,6 +93,8 @@ xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_page
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.v_scale = 1.0f;
   a.kv_format = xqa::kKvE5M2;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
   return a;
 }
 
@@ -309,6 +311,29 @@ xqa_status_t xqa_append_kv(xqa_handle_t h, const void* k_new, const void* v_new,
   a.max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
   hipError_t e = xqa::launch_append(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+  return XQA_OK;
+}
+
+xqa_status_t xqa_decode_append(xqa_handle_t h, const void* q, const void* k_new, const void* v_new,
+                               uint8_t* k_pages, uint8_t* v_pages, const int32_t* block_table,
+                               const int32_t* context_lens, int32_t batch, float scale, void* out,
+                               void* stream) {
+  xqa_status_t st =
+      check_decode_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
+  if (st != XQA_OK) return st;
+  if (!k_new || !v_new) return fail(XQA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(XQA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  if ((st = check_device(h)) != XQA_OK) return st;
+  xqa::AttendArgs a =
+      attend_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = xqa::launch_split(a, h->grid, s);
+  if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+  e = xqa::launch_combine(a, s);
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return XQA_OK;
 }
 

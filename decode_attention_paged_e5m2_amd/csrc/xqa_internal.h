@@ -86,6 +86,8 @@ struct AttendArgs {
   float scale_log2e;      // scale * k_scale * log2(e): scores are kept in base-2 units
   float v_scale;          // per-tensor V dequantisation scale, applied to the normalised rows
   int32_t kv_format;      // KvFormat
+  const uint16_t* k_new;  // fused KV append: new token rows [batch][Hkv][128] binary16,
+  const uint16_t* v_new;  //   written into k_pages / v_pages (E5M2); null: no append
 };
 
 // KV append: each sequence's new token (binary16 K and V rows for every KV

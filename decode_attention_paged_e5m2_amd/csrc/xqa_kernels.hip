@@ -83,6 +83,21 @@ __device__ __forceinline__ uint32_t widen_hi(uint32_t x) {   // codes 2, 3 of x
   return __builtin_amdgcn_perm(0u, x, 0x030C020Cu);
 }
 
+// E5M2 code of a binary16 value. E5M2 is the high byte of binary16 (same
+// sign, exponent field and bias), so rounding the 16-bit pattern to its high
+// byte, to nearest even, is exact rounding of the value; subnormals and the
+// carry into the exponent need no special case. Past the largest finite code
+// 0x7B (57344) the nearest finite value is 0x7B: saturation, infinities
+// included. NaN gives 0x7F. The sign is kept.
+__device__ __forceinline__ uint32_t e5m2_from_f16(uint32_t h) {
+  const uint32_t sign = (h >> 8) & 0x80u;
+  const uint32_t mag = h & 0x7FFFu;
+  uint32_t r = (mag + 0x7Fu + ((mag >> 8) & 1u)) >> 8;
+  r = r > 0x7Bu ? 0x7Bu : r;
+  r = mag > 0x7C00u ? 0x7Fu : r;
+  return sign | r;
+}
+
 // E4M3 (OCP, bias 7): two codes of x -> two binary16 values with the gfx950
 // conversion instruction at scale 1. Every E4M3 value is a binary16 value,
 // so this is exact (checked for all 256 codes through xqa_debug_widen_e4m3).
@@ -414,6 +429,39 @@ __device__ __forceinline__ void process_block(RawBlock& r, const half8 (&qf)[4],
   }
 }
 
+// Sixteen binary16 values (x0: values 0..7, x1: 8..15) -> their sixteen
+// E5M2 codes, in memory order.
+__device__ __forceinline__ u32x4 e5m2_pack16(const u32x4& x0, const u32x4& x1) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t p0 = w < 2 ? x0[2 * w] : x1[2 * (w - 2)];
+    const uint32_t p1 = w < 2 ? x0[2 * w + 1] : x1[2 * (w - 2) + 1];
+    r[w] = e5m2_from_f16(p0 & 0xFFFFu) | (e5m2_from_f16(p0 >> 16) << 8) |
+           (e5m2_from_f16(p1 & 0xFFFFu) << 16) | (e5m2_from_f16(p1 >> 16) << 24);
+  }
+  return r;
+}
+
+// Fused KV append: writes the new token's E5M2 K and V rows (binary16 rows
+// of k_new / v_new for sequence b, KV head h) to slot `row` of page
+// page_id. One wave, 16 bytes per lane per row: lane l < 8 encodes K bytes
+// [16l, 16l + 16), lanes 8..15 the V bytes. The same wave later reads the
+// slot with its ordinary loads of the page, which observe its own earlier
+// stores; no other wave reads the slot.
+__device__ __forceinline__ void append_store(const AttendArgs& a, int b, int h, int page_id, int row,
+                                             int lane) {
+  if (lane >= 16) return;
+  const int part = lane & 7;
+  const bool is_v = lane >= 8;
+  const long long src = ((long long)b * a.num_kv_heads + h) * kHeadDim + 16 * part;
+  const uint16_t* x = (is_v ? a.v_new : a.k_new) + src;
+  const u32x4 codes = e5m2_pack16(*(const u32x4*)x, *(const u32x4*)(x + 8));
+  uint8_t* pages = const_cast<uint8_t*>(is_v ? a.v_pages : a.k_pages);
+  *(u32x4*)(pages + ((size_t)page_id * a.num_kv_heads + h) * kPageHeadBytes +
+            (size_t)row * kHeadDim + 16 * part) = codes;
+}
+
 // Output row of query row r (token r / G, head h * G + r % G) of sequence b:
 // out is [batch][M][Hq][head_dim].
 __device__ __forceinline__ uint16_t* out_row(const AttendArgs& a, int b, int h, int r) {
@@ -432,7 +480,7 @@ struct SplitShared {
 // min(n, 32 jb_hi)) for KV head h. The four waves take interleaved blocks,
 // then merge in LDS. `direct`: the segment is the whole sequence, so the
 // normalised output is written; otherwise the state goes to `rec`.
-template <int F>
+template <int F, bool kAppend>
 __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh, int b, int h,
                                             int n, int jb_lo, int jb_hi, bool direct, float* rec,
                                             int lane, int wave) {
@@ -489,6 +537,17 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
   // The wave's blocks are j = wave + 4m. Page ids are fetched 32 blocks at a
   // time with one vector load (lane i: block m = i/2, page (i&1)) and read
   // out with v_readlane, so address generation never waits on a scalar miss.
+  // Fused append: the new token n - 1 lies in this segment's last block
+  // unless the length was clamped to the table's capacity (then nothing is
+  // written). The wave that will read that block writes the new rows into
+  // the page first; its loads of the block then see them.
+  if constexpr (kAppend) {
+    if (t_end == n && (n < a.max_tokens || a.context_lens[b] == n) &&
+        ((n - 1 - t_begin) / kBlockTokens) % kWaves == wave) {
+      append_store(a, b, h, bt[(n - 1) / kPageSize], (n - 1) % kPageSize, lane);
+    }
+  }
+
   for (int c0 = 0; c0 < my_blocks; c0 += 32) {
     int pg = first_page + 2 * (wave + kWaves * (c0 + (lane >> 1))) + (lane & 1);
     pg = min(pg, last_page);   // blocks past the end read a valid page; masked later
@@ -578,7 +637,9 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
   __syncthreads();   // the LDS state is reused by the next segment
 }
 
-template <int F>
+// kAppend: the fused KV append (E5M2 only); a separate instantiation so that
+// plain decode carries none of its registers.
+template <int F, bool kAppend>
 __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
   __shared__ SplitShared sh;
   const int lane = threadIdx.x & 63;
@@ -602,8 +663,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
     const long long seg_hi = hi < sq.off + nb ? hi : sq.off + nb;
     const bool direct = item_of_block(sq.off, NB, P) == item_of_block(sq.off + nb - 1, NB, P);
     float* rec = a.partials + ((long long)(2 * item + (first ? 0 : 1)) * Hkv + h) * a.item_stride;
-    run_segment<F>(a, sh, sq.b, h, sq.n, (int)(seg_lo - sq.off), (int)(seg_hi - sq.off), direct,
-                   rec, lane, wave);
+    run_segment<F, kAppend>(a, sh, sq.b, h, sq.n, (int)(seg_lo - sq.off), (int)(seg_hi - sq.off),
+                            direct, rec, lane, wave);
     if (sq.off + nb >= hi) break;
     first = false;
     do {   // next non-empty sequence (one exists: this item has blocks left)
@@ -695,21 +756,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) 
 }
 
 // ---------------------------------------------------------------- KV append
-// E5M2 code of a binary16 value. E5M2 is the high byte of binary16 (same
-// sign, exponent field and bias), so rounding the 16-bit pattern to its high
-// byte, to nearest even, is exact rounding of the value; subnormals and the
-// carry into the exponent need no special case. Past the largest finite code
-// 0x7B (57344) the nearest finite value is 0x7B: saturation, infinities
-// included. NaN gives 0x7F. The sign is kept.
-__device__ __forceinline__ uint32_t e5m2_from_f16(uint32_t h) {
-  const uint32_t sign = (h >> 8) & 0x80u;
-  const uint32_t mag = h & 0x7FFFu;
-  uint32_t r = (mag + 0x7Fu + ((mag >> 8) & 1u)) >> 8;
-  r = r > 0x7Bu ? 0x7Bu : r;
-  r = mag > 0x7C00u ? 0x7Fu : r;
-  return sign | r;
-}
-
 // One thread per (sequence, KV head, K or V, 8 head-dim values): a 16-byte
 // read of the new row, an 8-byte write into the page slot. 16 consecutive
 // threads cover one 128-value row, so reads and writes are contiguous.
@@ -765,10 +811,12 @@ __global__ void widen_kernel(const uint8_t* in, uint16_t* out16, float* out32, l
 }  // namespace
 
 hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream) {
-  if (a.kv_format == kKvE4M3) {
-    hipLaunchKernelGGL(split_kernel<kKvE4M3>, dim3(grid), dim3(kThreads), 0, stream, a);
+  if (a.k_new != nullptr) {
+    hipLaunchKernelGGL((split_kernel<kKvE5M2, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  } else if (a.kv_format == kKvE4M3) {
+    hipLaunchKernelGGL((split_kernel<kKvE4M3, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(split_kernel<kKvE5M2>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((split_kernel<kKvE5M2, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -802,14 +850,19 @@ hipError_t launch_widen(const uint8_t* in, uint16_t* out_f16, float* out_f32, in
   return hipGetLastError();
 }
 
-// Resident split workgroups per CU: the smaller of the two formats' figures,
-// so one grid serves both.
+// Resident split workgroups per CU: the smallest figure of the three
+// instantiations, so one grid serves all of them.
 hipError_t attend_blocks_per_cu(int* blocks) {
-  int a = 0, b = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, split_kernel<kKvE5M2>, kThreads, 0);
+  int a = 0, b = 0, c = 0;
+  hipError_t e =
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, split_kernel<kKvE5M2, false>, kThreads, 0);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, split_kernel<kKvE4M3, false>, kThreads, 0);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, split_kernel<kKvE5M2, true>, kThreads, 0);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, split_kernel<kKvE4M3>, kThreads, 0);
   *blocks = a < b ? a : b;
+  if (c < *blocks) *blocks = c;
   return e;
 }
 

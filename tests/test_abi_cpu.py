@@ -77,6 +77,8 @@ def test_null_arguments_are_rejected(lib):
     assert lib.xqa_decode_fp8(null, 1, *args[1:7], 1, ctypes.c_float(0.1), ctypes.c_float(1.0),
                               ctypes.c_float(1.0), null, null) == 1
     assert lib.xqa_debug_widen_e4m3(null, null, null, 4, null) == 1
+    assert lib.xqa_decode_append(null, null, null, null, null, null, null, null, 1,
+                                 ctypes.c_float(0.1), null, null) == 1
     assert lib.xqa_decode_combine(null, null, 1, null, null) == 1
     assert lib.xqa_append_kv(null, null, null, null, null, 1, null, null, null) == 1
     assert lib.xqa_get_info(null, None) == 1

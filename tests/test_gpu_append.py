@@ -164,3 +164,75 @@ def test_append_and_decode_in_one_graph():
         torch.cuda.synchronize()
         assert torch.equal(got_k, dev.k_pages) and torch.equal(got_v, dev.v_pages), f"replay {i}"
         assert torch.equal(got_out.view(torch.int16), out.view(torch.int16)), f"replay {i}"
+
+
+@pytest.mark.parametrize("per_head", [0, 1, 3])
+def test_fused_append_decode_is_bitwise_append_then_decode(per_head):
+    # xqa_decode_append == xqa_append_kv; xqa_decode, bit for bit (output and
+    # pools): slot 0, slot 15, block edges, the table's capacity, a length
+    # past it (clamped, nothing written), empty and negative lengths, and long
+    # sequences whose last block falls in later 32-block chunks of a wave.
+    cap_pages = 330
+    lens = [1, 16, 17, 32, 33, 64, 0, -3, cap_pages * 16 + 9, 300, 5000, cap_pages * 16]
+    alloc = [max(0, min(n, cap_pages * 16)) for n in lens]
+    w = make_custom(alloc, 4, 32, [27, per_head], pool_pages=1400, max_pages_per_seq=cap_pages)
+    rng = np.random.default_rng(28 + per_head)
+    k_new = _dev((rng.standard_normal((w.batch, 4, 128)) * 3).astype(np.float16))
+    v_new = _dev(rng.standard_normal((w.batch, 4, 128)).astype(np.float16))
+    lens_t = _dev(np.asarray(lens, dtype=np.int32))
+    xqa = Xqa(max_batch=w.batch, num_q_heads=32, num_kv_heads=4, max_pages_per_seq=cap_pages,
+              max_work_items=4 * per_head)
+    sep, fused = to_device(w), to_device(w)
+    xqa.append_kv(k_new=k_new, v_new=v_new, block_table=sep.block_table, context_lens=lens_t,
+                  k_pages=sep.k_pages, v_pages=sep.v_pages)
+    out_sep = xqa.decode(q=sep.q, k_pages=sep.k_pages, v_pages=sep.v_pages,
+                         block_table=sep.block_table, context_lens=lens_t, scale=w.scale)
+    out_fused = xqa.decode_append(q=fused.q, k_new=k_new, v_new=v_new, k_pages=fused.k_pages,
+                                  v_pages=fused.v_pages, block_table=fused.block_table,
+                                  context_lens=lens_t, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out_fused.view(torch.int16), out_sep.view(torch.int16))
+    assert torch.equal(fused.k_pages, sep.k_pages) and torch.equal(fused.v_pages, sep.v_pages)
+    kp, vp = w.pools()
+    kr, vr = oracle.append_kv(kp, vp, w.block_table, np.asarray(lens), k_new.cpu().numpy(),
+                              v_new.cpu().numpy())
+    ref = oracle.decode_attention(w.q, kr, vr, w.block_table, np.asarray(lens), w.scale)
+    assert_parity(out_fused.float().cpu().numpy(), ref, f"fused append per_head={per_head}")
+
+
+def test_fused_append_decode_in_a_graph():
+    lens0 = np.array([40, 7, 300, 1, 1023], dtype=np.int64)
+    w = make_custom((lens0 + 8).tolist(), 4, 32, [29, 0], pool_pages=200)
+    rng = np.random.default_rng(30)
+    xqa = Xqa(max_batch=w.batch, num_q_heads=32, num_kv_heads=4,
+              max_pages_per_seq=w.max_pages_per_seq)
+    a, b = to_device(w), to_device(w)
+    k_new = torch.empty((w.batch, 4, 128), dtype=torch.float16, device="cuda:0")
+    v_new = torch.empty_like(k_new)
+    lens = torch.empty(w.batch, dtype=torch.int32, device="cuda:0")
+    out_a = torch.empty_like(a.q)
+    out_b = torch.empty_like(b.q)
+
+    def fused():
+        xqa.decode_append(q=a.q, k_new=k_new, v_new=v_new, k_pages=a.k_pages, v_pages=a.v_pages,
+                          block_table=a.block_table, context_lens=lens, scale=w.scale, out=out_a)
+
+    torch.cuda.synchronize()
+    lens.copy_(torch.from_numpy((lens0 + 1).astype(np.int32)))
+    fused()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fused()
+    for i in range(10):
+        k_new.copy_(torch.from_numpy(rng.standard_normal((w.batch, 4, 128)).astype(np.float16)))
+        v_new.copy_(torch.from_numpy(rng.standard_normal((w.batch, 4, 128)).astype(np.float16)))
+        lens.copy_(torch.from_numpy((lens0 + 1 + (i % 8)).astype(np.int32)))
+        torch.cuda.synchronize()
+        g.replay()
+        xqa.append_kv(k_new=k_new, v_new=v_new, block_table=b.block_table, context_lens=lens,
+                      k_pages=b.k_pages, v_pages=b.v_pages)
+        xqa.decode(q=b.q, k_pages=b.k_pages, v_pages=b.v_pages, block_table=b.block_table,
+                   context_lens=lens, scale=w.scale, out=out_b)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16)), f"replay {i}"
+        assert torch.equal(a.k_pages, b.k_pages) and torch.equal(a.v_pages, b.v_pages), f"replay {i}"
