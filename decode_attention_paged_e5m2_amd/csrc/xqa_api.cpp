@@ -4,6 +4,7 @@
 // exponents" asks of admission code in its audit comments: explicit errors,
 // never a silent no-launch, no environment reads in native code).
 
+#include <algorithm>
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
@@ -19,6 +20,7 @@ struct xqa_handle_s {
   int grid;          // split workgroups = work-item capacity
   int per_head;      // grid / Hkv
   int item_stride;   // floats per partial record
+  int combine_waves; // waves per combine workgroup
   float* partials;   // workspace: grid partial records
   size_t workspace_bytes;
 };
@@ -90,6 +92,7 @@ xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_page
   a.max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
   a.per_head = h->per_head;
   a.item_stride = h->item_stride;
+  a.combine_waves = h->combine_waves;
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.v_scale = 1.0f;
   a.kv_format = xqa::kKvE5M2;
@@ -155,6 +158,15 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
     // Every item resident at once: one round of equal-sized items, the same
     // number on every CU.
     grid = (long long)cus * per_cu;
+    // A step never has more than max_batch full sequences, so it never plans
+    // more than ceil(NB_max / 8) items per head; slots past that would only
+    // be dispatched to exit (a few microseconds on small workloads).
+    const long long nb_max =
+        (long long)cfg->max_batch *
+        xqa::seq_blocks((int32_t)((long long)cfg->max_pages_per_seq * xqa::kPageSize));
+    const long long useful = (long long)cfg->num_kv_heads *
+                             ((nb_max + xqa::kMinItemBlocks - 1) / xqa::kMinItemBlocks);
+    if (grid > useful) grid = useful;
     if (grid < min_grid) grid = min_grid;
     if (grid > max_grid) grid = max_grid;
   }
@@ -173,6 +185,12 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
   h->grid = (int)grid;
   h->per_head = per_head;
   h->item_stride = stride;
+  // A sequence leaves at most one split state per item and per block, so a
+  // handle whose bound stays within one combine round gets the one-wave
+  // combine workgroups; a longer one shares the rounds over four waves.
+  const int max_states = std::min(per_head, xqa::seq_blocks(
+      (int32_t)((long long)cfg->max_pages_per_seq * xqa::kPageSize)));
+  h->combine_waves = max_states > xqa::kCombineRound ? xqa::kCombineMaxWaves : 1;
   h->workspace_bytes = ws;
   h->partials = nullptr;
   e = hipMalloc(reinterpret_cast<void**>(&h->partials), ws);

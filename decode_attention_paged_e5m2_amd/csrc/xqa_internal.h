@@ -17,9 +17,8 @@ constexpr int kMinItemBlocks = 8;                      // smallest work item: 8 
 constexpr int kMaxItemsPerHead = 2048;                 // bound on work items per KV head
 constexpr int kMaxSeqTokens = 1 << 24;                 // bound on max_pages_per_seq * page_size
 constexpr int kMaxBatch = 1 << 16;                     // bound on max_batch
-constexpr int kCombineThreads = 64;                    // one wave per combine workgroup
-constexpr int kCombineChunks = 8;                      // combine workgroups per (sequence, KV head)
 constexpr int kCombineRound = 16;                      // split states loaded per round
+constexpr int kCombineMaxWaves = 4;                    // waves per combine workgroup (1 or 4)
 
 // ---------------------------------------------------------------------------
 // The balanced plan. Every workgroup of both kernels evaluates it on the
@@ -83,6 +82,7 @@ struct AttendArgs {
   int32_t max_tokens;
   int32_t per_head;       // grid / Hkv
   int32_t item_stride;    // floats per partial record
+  int32_t combine_waves;  // 1: no sequence can leave more than kCombineRound states; else 4
   float scale_log2e;      // scale * k_scale * log2(e): scores are kept in base-2 units
   float v_scale;          // per-tensor V dequantisation scale, applied to the normalised rows
   int32_t kv_format;      // KvFormat

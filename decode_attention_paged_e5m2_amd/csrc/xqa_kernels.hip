@@ -51,8 +51,10 @@
 //
 // The combine kernel then merges the states of every split sequence with
 // the exact log-sum-exp rule M = max m_s, L = sum l_s 2^(m_s-M),
-// out = v_scale * sum 2^(m_s-M) O_s / L (split order, in rounds of
-// kCombineRound states), and writes the zero rows of empty sequences.
+// out = v_scale * sum 2^(m_s-M) O_s / L (in rounds of kCombineRound states;
+// a long sequence's rounds are shared out over the workgroup's four waves,
+// whose partial merges then meet in LDS in a fixed order), and writes the
+// zero rows of empty sequences.
 // The kernel boundary makes the split states visible across the chip's
 // separately cached dies without any in-kernel cache write-back.
 //
@@ -674,30 +676,73 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
 }
 
 // ----------------------------------------------------------- combine kernel
-// One single-wave workgroup per (sequence, KV head, 16-column chunk): a long
-// sequence's many split states are read by kCombineChunks CUs at once. Lane
-// t owns columns 2(t%8), 2(t%8)+1 of the chunk for query head t/8 and reads
-// exactly that slice of every split state, kCombineRound states per round
-// with all loads issued before any is used: one memory round trip per round
-// (one for most sequences) and no cross-lane reduction.
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) {
+// Workgroups of W waves (W = 1, or 4 when a sequence can leave more states
+// than one round holds) merge each sequence's split states with the
+// log-sum-exp rule, reading states in rounds of kCombineRound with every load
+// of a round issued before any is used. A workgroup covers 16 W columns of
+// one (sequence, KV head); 128 / (16 W) workgroups cover the head.
+//
+// Up to one round of states (most sequences), or W = 1: wave w owns 16
+// columns, lane t the columns 2(t%8), 2(t%8)+1 of query row t/8; one memory
+// round trip per round and no cross-lane step.
+//
+// More states with W = 4 (a long sequence split over many items): the four
+// waves split the rounds (wave w takes rounds w, w+4, ...), lane t owning 8
+// columns of row t/8 across the workgroup's 64; the four partial merges then
+// meet in LDS in wave order. The split depends on the state count only, so
+// the result is the same on every run.
+
+// Merges one round of split states (cnt valid entries) into (M, L, o[0..N)).
+// A state of a query row that saw no token has m = -inf and weight 0; equal
+// maxima keep the sums unscaled.
+template <int N>
+__device__ __forceinline__ void merge_round(const float (&mv)[kCombineRound],
+                                            const float (&lv)[kCombineRound],
+                                            const float (&ov)[kCombineRound][N], int cnt,
+                                            float& M, float& L, float (&o)[N]) {
+  float mr = M;
+#pragma unroll
+  for (int k = 0; k < kCombineRound; ++k) mr = fmaxf(mr, k < cnt ? mv[k] : -INFINITY);
+  const float fa = M == mr ? 1.f : exp2_fast(M - mr);   // 0 on the first round
+  L *= fa;
+#pragma unroll
+  for (int c = 0; c < N; ++c) o[c] *= fa;
+  M = mr;
+#pragma unroll
+  for (int k = 0; k < kCombineRound; ++k) {
+    const float w = (k < cnt && mv[k] != -INFINITY) ? exp2_fast(mv[k] - M) : 0.f;
+    L += w * lv[k];
+#pragma unroll
+    for (int c = 0; c < N; ++c) o[c] += w * ov[k][c];
+  }
+}
+
+struct CombineShared {
+  float m[kCombineMaxWaves][kMaxGroup * 8];
+  float l[kCombineMaxWaves][kMaxGroup * 8];
+  float4v o[kCombineMaxWaves][kMaxGroup * 8][2];
+};
+
+template <int W>
+__global__ __launch_bounds__(64 * W) void combine_kernel(AttendArgs a) {
+  constexpr int kWgCols = 16 * W;
+  constexpr int kChunks = kHeadDim / kWgCols;
   const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int R = a.rows;
   const int Hkv = a.num_kv_heads;
-  const int chunk = blockIdx.x % kCombineChunks;
-  const int bh = blockIdx.x / kCombineChunks;
+  const int chunk = blockIdx.x % kChunks;
+  const int bh = blockIdx.x / kChunks;
   const int b = bh / Hkv;
   const int h = bh % Hkv;
-  constexpr int kCols = kHeadDim / kCombineChunks;   // 16 columns per chunk
-  constexpr int kPairs = kCols / 2;                  // lanes per query row
 
   const SeqTable seqs(a.context_lens, a.batch, a.max_tokens, lane);
   const long long NB = seqs.nb;
   const int P = items_per_head(NB, a.per_head);
   const SeqInfo sq = seqs.at(b, lane);
   if (sq.n == 0) {
-    for (int e = threadIdx.x; e < R * kPairs; e += kCombineThreads) {
-      *(uint32_t*)(out_row(a, b, h, e / kPairs) + chunk * kCols + (e % kPairs) * 2) = 0;
+    for (int e = threadIdx.x; e < R * (kWgCols / 2); e += 64 * W) {
+      *(uint32_t*)(out_row(a, b, h, e / (kWgCols / 2)) + chunk * kWgCols + (e % (kWgCols / 2)) * 2) = 0;
     }
     return;
   }
@@ -713,45 +758,86 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttendArgs a) 
     return a.partials + ((long long)slot * Hkv + h) * a.item_stride;
   };
 
-  for (int e = threadIdx.x; e < R * kPairs; e += kCombineThreads) {
-    const int gg = e / kPairs;
-    const int c = chunk * kCols + (e % kPairs) * 2;   // first of this lane's two columns
-    const int col = gg * kHeadDim + c;
-    float M = -INFINITY, Ls = 0.f;
-    float o0 = 0.f, o1 = 0.f;
-    for (int s0 = 0; s0 < nsb; s0 += kCombineRound) {
-      const int cnt = min(kCombineRound, nsb - s0);
-      float mv[kCombineRound], lv[kCombineRound];
-      float2 ov[kCombineRound];
-      // Unconditional loads (slots past the last split re-read it and are
-      // masked below), so the whole round is in flight at once.
+  if (W == 1 || nsb <= kCombineRound) {
+    // With W = 1 the handle bounds the state count by kCombineRound, so
+    // every instantiation merges a single round here.
+    for (int e = lane; e < R * 8; e += 64) {
+      const int gg = e >> 3;
+      const int c = chunk * kWgCols + 16 * wave + (e & 7) * 2;
+      float mv[kCombineRound], lv[kCombineRound], ov[kCombineRound][2];
+      // Unconditional loads (slots past the last state re-read it and are
+      // masked in the merge), so the whole round is in flight at once.
 #pragma unroll
       for (int k = 0; k < kCombineRound; ++k) {
-        const float* r = rec(min(s0 + k, nsb - 1));
-        ov[k] = *(const float2*)(r + col);
+        const float* r = rec(min(k, nsb - 1));
+        const float2 v = *(const float2*)(r + gg * kHeadDim + c);
+        ov[k][0] = v.x;
+        ov[k][1] = v.y;
         mv[k] = r[mo + gg];
         lv[k] = r[mo + R + gg];
       }
-      float mr = M;
-#pragma unroll
-      for (int k = 0; k < kCombineRound; ++k) mr = fmaxf(mr, k < cnt ? mv[k] : -INFINITY);
-      // Rescales earlier rounds (0 on the first). A state of a query row
-      // that saw no token has m = -inf and weight 0; equal maxima keep the sums.
-      const float fa = M == mr ? 1.f : exp2_fast(M - mr);
-      Ls *= fa;
-      o0 *= fa;
-      o1 *= fa;
-      M = mr;
-#pragma unroll
-      for (int k = 0; k < kCombineRound; ++k) {
-        const float w = (k < cnt && mv[k] != -INFINITY) ? exp2_fast(mv[k] - M) : 0.f;
-        Ls += w * lv[k];
-        o0 += w * ov[k].x;
-        o1 += w * ov[k].y;
-      }
+      float M = -INFINITY, L = 0.f, o[2] = {0.f, 0.f};
+      merge_round<2>(mv, lv, ov, min(nsb, kCombineRound), M, L, o);
+      const float inv = L > 0.f ? a.v_scale / L : 0.f;   // a row with no visible token is zero
+      *(uint32_t*)(out_row(a, b, h, gg) + c) = pack_half2(o[0] * inv, o[1] * inv);
     }
-    const float inv = Ls > 0.f ? a.v_scale / Ls : 0.f;   // a row with no visible token is zero
-    *(uint32_t*)(out_row(a, b, h, gg) + c) = pack_half2(o0 * inv, o1 * inv);
+    return;
+  }
+
+  if constexpr (W > 1) {
+    __shared__ CombineShared sh;
+    // Wave w merges rounds w, w + W, ...; lane entry e: row e/8, columns
+    // 64 chunk + 8(e%8) .. +8.
+    for (int e = lane; e < R * 8; e += 64) {
+      const int gg = e >> 3;
+      const int c = chunk * kWgCols + (e & 7) * 8;
+      float M = -INFINITY, L = 0.f;
+      float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int s0 = kCombineRound * wave; s0 < nsb; s0 += kCombineRound * W) {
+        float mv[kCombineRound], lv[kCombineRound], ov[kCombineRound][8];
+#pragma unroll
+        for (int k = 0; k < kCombineRound; ++k) {
+          const float* r = rec(min(s0 + k, nsb - 1));
+          const float4v v0 = *(const float4v*)(r + gg * kHeadDim + c);
+          const float4v v1 = *(const float4v*)(r + gg * kHeadDim + c + 4);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            ov[k][x] = v0[x];
+            ov[k][4 + x] = v1[x];
+          }
+          mv[k] = r[mo + gg];
+          lv[k] = r[mo + R + gg];
+        }
+        merge_round<8>(mv, lv, ov, min(kCombineRound, nsb - s0), M, L, o);
+      }
+      sh.m[wave][e] = M;   // -inf and 0 for a wave with no rounds
+      sh.l[wave][e] = L;
+      sh.o[wave][e][0] = float4v{o[0], o[1], o[2], o[3]};
+      sh.o[wave][e][1] = float4v{o[4], o[5], o[6], o[7]};
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < R * 8; e += 64 * W) {
+      float M = sh.m[0][e];
+#pragma unroll
+      for (int w = 1; w < W; ++w) M = fmaxf(M, sh.m[w][e]);
+      float L = 0.f;
+      float4v o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float mw = sh.m[w][e];
+        const float f = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
+        L += f * sh.l[w][e];
+        o0 += f * sh.o[w][e][0];
+        o1 += f * sh.o[w][e][1];
+      }
+      const float inv = L > 0.f ? a.v_scale / L : 0.f;
+      uint4 packed;
+      packed.x = pack_half2(o0[0] * inv, o0[1] * inv);
+      packed.y = pack_half2(o0[2] * inv, o0[3] * inv);
+      packed.z = pack_half2(o1[0] * inv, o1[1] * inv);
+      packed.w = pack_half2(o1[2] * inv, o1[3] * inv);
+      *(uint4*)(out_row(a, b, h, e >> 3) + chunk * kWgCols + (e & 7) * 8) = packed;
+    }
   }
 }
 
@@ -822,8 +908,14 @@ hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const AttendArgs& a, hipStream_t stream) {
-  const int grid = a.batch * a.num_kv_heads * kCombineChunks;
-  hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kCombineThreads), 0, stream, a);
+  if (a.combine_waves == kCombineMaxWaves) {
+    constexpr int W = kCombineMaxWaves;
+    const int grid = a.batch * a.num_kv_heads * (kHeadDim / (16 * W));
+    hipLaunchKernelGGL(combine_kernel<W>, dim3(grid), dim3(64 * W), 0, stream, a);
+  } else {
+    const int grid = a.batch * a.num_kv_heads * (kHeadDim / 16);
+    hipLaunchKernelGGL(combine_kernel<1>, dim3(grid), dim3(64), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -73,8 +73,10 @@ typedef struct {
   int32_t head_dim;          /* 128                                                     */
   int32_t page_size;         /* 16                                                      */
   int32_t max_pages_per_seq; /* >= 1: block-table row stride in int32 elements          */
-  int32_t max_work_items;    /* 0: sized from the device's occupancy; else the split    */
-                             /* grid in workgroups, in [Hkv, Hkv*2048]                  */
+  int32_t max_work_items;    /* 0: sized from the device's occupancy (every CU's        */
+                             /* resident slots), capped at the most items the largest   */
+                             /* step the handle accepts can use; else the split grid    */
+                             /* in workgroups, in [Hkv, Hkv*2048]                       */
   int32_t max_query_tokens;  /* 0 or 1: one query token per sequence; up to M with      */
                              /* G * M <= 16 for xqa_decode_multi                        */
 } xqa_config_t;

@@ -121,6 +121,40 @@ def test_work_item_boundaries():
         assert_parity(out, reference(w), f"aligned items shift={shift}")
 
 
+def _states_of(ctx, b, per_head):
+    # Split states sequence b leaves, from the plan's published formulas:
+    # 32-token blocks, P = min(per_head, ceil(NB / 8)) items of equal size.
+    nb = [-(-max(int(n), 0) // 32) for n in ctx]
+    NB = sum(nb)
+    P = min(per_head, -(-NB // 8))
+    off = sum(nb[:b])
+    item = lambda x: ((x + 1) * P + NB - 1) // NB - 1
+    return item(off + nb[b] - 1) - item(off) + 1
+
+
+@pytest.mark.parametrize("hkv,hq", [(1, 8), (1, 16), (2, 6)])
+def test_combine_state_counts(hkv, hq):
+    # One long sequence between two short ones, split over 15 to 129 work
+    # items: a single round of split states, then several rounds shared out
+    # over the combine's waves (some waves with none), with 8, 16 and 3 query
+    # rows per KV head.
+    rng = np.random.default_rng(77 + hq)
+    seen = []
+    for per_head in (15, 16, 17, 18, 33, 34, 66, 100, 130):
+        n = per_head * 8 * 32 + int(rng.integers(0, 256))
+        ctx = [300, n, 50]
+        pages = -(-n // 16)
+        xqa = Xqa(max_batch=3, num_q_heads=hq, num_kv_heads=hkv, max_pages_per_seq=pages,
+                  max_work_items=hkv * per_head)
+        w = make_custom(ctx, hkv, hq, [78, hq, per_head], max_pages_per_seq=pages)
+        out, _, _ = run(w, xqa=xqa)
+        nsb = _states_of(ctx, 1, per_head)
+        seen.append(nsb)
+        st = assert_parity(out, reference(w), f"hkv={hkv} hq={hq} states={nsb}")
+        log(f"combine hkv={hkv} hq={hq} per_head={per_head} states={nsb}", st)
+    assert min(seen) <= 16 and any(17 <= x <= 20 for x in seen) and max(seen) > 128
+
+
 @pytest.mark.parametrize("batch,per_head", [(65, 0), (129, 5), (700, 0), (700, 3)])
 def test_large_batches(batch, per_head):
     # More than 64 sequences: the plan scans context_lens 64 sequences at a
