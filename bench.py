@@ -82,7 +82,7 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=0, help="oracle repetitions (0 = auto, ~10-20 s)")
     ap.add_argument("--quick", action="store_true", help="skip A/B/B/A and warm-mode extras")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the multi-token, E4M3 and KV-append legs (profiling runs)")
+                    help="skip the floor, multi-token, E4M3 and KV-append legs (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (5x), the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counter readings")
@@ -93,15 +93,47 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def gpu_clocks():
+    """Current GPU clocks and power as rocm-smi reports them (a child process), or None."""
+    import subprocess
+    try:
+        res = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                             capture_output=True, text=True, timeout=30)
+        data = json.loads(res.stdout)
+        card = next(iter(v for k, v in data.items() if k.startswith("card")))
+        return {k: v for k, v in card.items() if "clock" in k.lower() or "power" in k.lower()}
+    except Exception:
+        return None
+
+
+def host_cpu():
+    """CPU model and BLAS library of the host, for the oracle baseline."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", 1
+    try:
+        from threadpoolctl import threadpool_info
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = max(p.get("num_threads", 1) for p in info)
+    except Exception:
+        pass
+    return model, blas, threads
+
+
 def cpu_baseline_leg(w, gpu_out, reps_arg):
     """Time the float64 oracle on a full decode step; compare it with gpu_out."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    model, blas, threads = host_cpu()
     kp, vp = w.pools()
     t = time.perf_counter()
     ref = oracle.decode_attention(w.q, kp, vp, w.block_table, w.context_lens, w.scale)
@@ -113,7 +145,8 @@ def cpu_baseline_leg(w, gpu_out, reps_arg):
     cpu_s = (time.perf_counter() - t) / reps
     cpu = {"value": w.kv_bytes / cpu_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
            "sample": f"full decode step of {w.name} (sum ctx={w.total_tokens}, {w.kv_bytes} KV bytes), "
-                     f"{reps} repetitions, {cpu_s * 1e6:.0f} us/step; float64 numpy, BLAS threads={threads}"}
+                     f"{reps} repetitions, {cpu_s * 1e6:.0f} us/step; float64 numpy, "
+                     f"BLAS {blas} with {threads} threads; CPU {model}"}
     log(f"cpu oracle: {cpu_s * 1e3:.1f} ms/step ({cpu['value']:.3f} GB/s) x{reps}")
     # tolerance: |gpu - ref| <= 2e-3 or <= 1e-2 |ref| per element; relative L2 <= 1e-3
     err = np.abs(gpu_out.astype(np.float64) - ref)
@@ -136,6 +169,7 @@ def main():
     import numpy as np
     import torch
 
+    clocks_before = gpu_clocks()
     from decode_attention_paged_e5m2_amd import Xqa
     from workloads import make_config
     from workloads.device import to_device
@@ -281,7 +315,33 @@ def main():
     log(f"1-step graph replay: {us_1:.2f} us/step")
 
     detail = {"us_per_step_graph_Rstep": us_step, "us_per_step_graph_1step": us_1,
-              "kv_bytes_per_step_mean": statistics.mean(kv_bytes), "handle": info}
+              "kv_bytes_per_step_mean": statistics.mean(kv_bytes), "handle": info,
+              "gpu_clocks_before": clocks_before}
+
+    if not args.no_extras:
+        # Floor: the same R-step graph with every context length 0 (launches,
+        # plan, zero rows), the fixed cost under each step.
+        zero_lens = [torch.zeros_like(d.context_lens) for d in devs]
+        zero_outs = [torch.empty_like(d.q) for d in devs]
+        floor_g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(floor_g):
+            for d, z, o in zip(devs, zero_lens, zero_outs):
+                xqa.decode(q=d.q, k_pages=d.k_pages, v_pages=d.v_pages, block_table=d.block_table,
+                           context_lens=z, scale=w0.scale, out=o)
+        for _ in range(max(args.warmup // R, 2)):
+            floor_g.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps // R):
+            floor_g.replay()
+        torch.cuda.synchronize()
+        us_floor = (time.perf_counter() - t) / steps * 1e6
+        if not all(bool((o == 0).all()) for o in zero_outs):
+            print(json.dumps({"error": "zero-length step did not write zero rows"}))
+            return 1
+        log(f"floor (all lengths 0, same graph shape): {us_floor:.2f} us/step")
+        detail["floor_us_per_step_zero_lengths"] = us_floor
+        del floor_g
 
     # ------------------------------------------------------ A/B/B/A blocks
     if not args.quick:
@@ -468,6 +528,7 @@ def main():
         log(f"KV append: {append_us:.2f} us per launch; append + decode graph {us_full:.2f} us/step; "
             f"fused {us_fused:.2f} us/step")
 
+    detail["gpu_clocks_after"] = gpu_clocks()
     line = {
         "metric": METRIC,
         "value": gbs,

@@ -42,6 +42,7 @@ class XqaInfo(ctypes.Structure):
         ("threads_per_item", ctypes.c_int32),
         ("item_stride_floats", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64),
+        ("kernels_per_step", ctypes.c_int32),
     ]
 
 

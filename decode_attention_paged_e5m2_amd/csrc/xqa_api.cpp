@@ -21,6 +21,7 @@ struct xqa_handle_s {
   int per_head;      // grid / Hkv
   int item_stride;   // floats per partial record
   int combine_waves; // waves per combine workgroup
+  bool direct_only;  // no sequence can leave split states: one kernel per step
   float* partials;   // workspace: grid partial records
   size_t workspace_bytes;
 };
@@ -93,6 +94,7 @@ xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_page
   a.per_head = h->per_head;
   a.item_stride = h->item_stride;
   a.combine_waves = h->combine_waves;
+  a.zero_empty = h->direct_only ? 1 : 0;
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.v_scale = 1.0f;
   a.kv_format = xqa::kKvE5M2;
@@ -191,6 +193,10 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
   const int max_states = std::min(per_head, xqa::seq_blocks(
       (int32_t)((long long)cfg->max_pages_per_seq * xqa::kPageSize)));
   h->combine_waves = max_states > xqa::kCombineRound ? xqa::kCombineMaxWaves : 1;
+  // With one state per sequence at most, every sequence is finished in the
+  // split kernel, which then also writes the zero rows of empty sequences:
+  // a decode step is one kernel.
+  h->direct_only = max_states <= 1;
   h->workspace_bytes = ws;
   h->partials = nullptr;
   e = hipMalloc(reinterpret_cast<void**>(&h->partials), ws);
@@ -222,6 +228,7 @@ xqa_status_t xqa_get_info(xqa_handle_t h, xqa_info_t* info) {
   info->threads_per_item = xqa::kThreads;
   info->item_stride_floats = h->item_stride;
   info->workspace_bytes = (int64_t)h->workspace_bytes;
+  info->kernels_per_step = h->direct_only ? 1 : 2;
   return XQA_OK;
 }
 
@@ -297,6 +304,7 @@ xqa_status_t xqa_decode_fp8(xqa_handle_t h, xqa_kv_format_t kv_format, const voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = xqa::launch_split(a, h->grid, s);
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+  if (h->direct_only) return XQA_OK;
   e = xqa::launch_combine(a, s);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return XQA_OK;
@@ -350,6 +358,7 @@ xqa_status_t xqa_decode_append(xqa_handle_t h, const void* q, const void* k_new,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = xqa::launch_split(a, h->grid, s);
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+  if (h->direct_only) return XQA_OK;
   e = xqa::launch_combine(a, s);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return XQA_OK;

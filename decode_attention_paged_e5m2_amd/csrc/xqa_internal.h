@@ -83,6 +83,7 @@ struct AttendArgs {
   int32_t per_head;       // grid / Hkv
   int32_t item_stride;    // floats per partial record
   int32_t combine_waves;  // 1: no sequence can leave more than kCombineRound states; else 4
+  int32_t zero_empty;     // no sequence can be split: the split kernel writes the zero rows
   float scale_log2e;      // scale * k_scale * log2(e): scores are kept in base-2 units
   float v_scale;          // per-tensor V dequantisation scale, applied to the normalised rows
   int32_t kv_format;      // KvFormat

@@ -653,6 +653,25 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
   const int P = items_per_head(NB, a.per_head);
   const int item = blockIdx.x / Hkv;
   const int h = blockIdx.x % Hkv;
+  if (a.zero_empty) {
+    // No combine runs on this handle: the zero rows of empty sequences are
+    // written here. Wave w of item i takes the 64-sequence chunks
+    // 4i + w, 4i + w + 4 per_head, ...; each empty sequence's R rows are
+    // written by the whole wave, 16 bytes per lane per store.
+    const int R = a.rows;
+    for (int b0 = 64 * (kWaves * item + wave); b0 < a.batch; b0 += 64 * kWaves * a.per_head) {
+      const int bl = b0 + lane;
+      unsigned long long empty = __ballot(bl < a.batch && clamp_len(a.context_lens[bl], a.max_tokens) == 0);
+      while (empty) {
+        const int bz = b0 + __ffsll(empty) - 1;
+        empty &= empty - 1;
+        for (int e = lane; e < R * (kHeadDim / 8); e += 64) {
+          *(uint4*)(out_row(a, bz, h, e / (kHeadDim / 8)) + (e % (kHeadDim / 8)) * 8) =
+              make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  }
   if (item >= P) return;   // the whole workgroup leaves
   const long long lo = item_lo(item, NB, P);
   const long long hi = item_lo(item + 1, NB, P);

@@ -89,6 +89,9 @@ typedef struct {
   int32_t threads_per_item;  /* workgroup size of the split kernel                      */
   int32_t item_stride_floats;/* floats per split-state record (two records per item)    */
   int64_t workspace_bytes;   /* device bytes the handle owns                            */
+  int32_t kernels_per_step;  /* 2 (split + combine), or 1 when the handle's bounds keep  */
+                             /* every sequence in one work item (the split kernel then  */
+                             /* also writes the zero rows of empty sequences)           */
 } xqa_info_t;
 
 /* Create a handle on the current HIP device. Validates cfg, sizes the split
@@ -109,7 +112,8 @@ xqa_status_t xqa_destroy(xqa_handle_t handle);
 xqa_status_t xqa_get_info(xqa_handle_t handle, xqa_info_t* info);
 
 /* One decode step: the split kernel and the combine kernel, back to back on
- * `stream`. Nothing is allocated and nothing waits on the host, so the call
+ * `stream` (the split kernel alone when the handle's bounds keep every
+ * sequence in one work item; xqa_info_t.kernels_per_step). Nothing is allocated and nothing waits on the host, so the call
  * can be captured into a HIP graph and replayed with new contents of q,
  * block_table and context_lens. batch must be in [1, max_batch]; scale must
  * be finite. q, k_pages, v_pages and out must be 16-byte aligned,
@@ -162,7 +166,9 @@ xqa_status_t xqa_decode_fp8(xqa_handle_t handle, xqa_kv_format_t kv_format, cons
  * written to out; the others leave split states in the workspace. Same
  * arguments and errors as xqa_decode. xqa_decode_combine must follow on the
  * same stream, with the same context_lens, batch and out, before the handle
- * is used again. Exposed so the two stages can be timed or scheduled apart. */
+ * is used again. Exposed so the two stages can be timed or scheduled apart.
+ * On a handle with kernels_per_step 1 the split kernel also writes the zero
+ * rows, and the combine finds nothing left to do. */
 xqa_status_t xqa_decode_split(xqa_handle_t handle, const void* q, const uint8_t* k_pages,
                               const uint8_t* v_pages, const int32_t* block_table,
                               const int32_t* context_lens, int32_t batch, float scale,
