@@ -99,3 +99,30 @@ def test_split_handles_keep_two_kernels():
                max_pages_per_seq=4096).info["kernels_per_step"] == 2
     assert Xqa(max_batch=4, num_q_heads=32, num_kv_heads=4,
                max_pages_per_seq=64).info["kernels_per_step"] == 2
+
+
+def test_one_kernel_multi_token_rows():
+    # Two query tokens per sequence (16 rows per KV head) on a one-item-per-
+    # head handle: empty sequences, a length-1 sequence whose first token
+    # sees nothing, and ragged lengths, against the float64 oracle.
+    rng = np.random.default_rng(93)
+    ctx = rng.integers(2, 600, size=70)
+    ctx[[0, 5, 64, 69]] = 0
+    ctx[7] = 1
+    w = make_custom(ctx.tolist(), 2, 16, [94, 0], max_pages_per_seq=40)
+    xqa = Xqa(max_batch=w.batch, num_q_heads=16, num_kv_heads=2, max_pages_per_seq=40,
+              max_work_items=2, max_query_tokens=2)
+    assert xqa.info["kernels_per_step"] == 1
+    dev = to_device(w)
+    q = rng.standard_normal((w.batch, 2, 16, 128)).astype(np.float16)
+    qd = torch.from_numpy(q).to(dev.q.device)
+    out = torch.full_like(qd, float("nan"))
+    xqa.decode(q=qd, k_pages=dev.k_pages, v_pages=dev.v_pages, block_table=dev.block_table,
+               context_lens=dev.context_lens, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    kp, vp = w.pools()
+    ref = oracle.decode_attention_multi(q, kp, vp, w.block_table, w.context_lens, w.scale)
+    assert_parity(got, ref, "one-kernel multi-token")
+    assert (got[ctx == 0] == 0).all()
+    assert (got[7, 0] == 0).all()
