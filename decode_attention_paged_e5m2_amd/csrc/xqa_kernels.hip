@@ -54,7 +54,9 @@
 // out = v_scale * sum 2^(m_s-M) O_s / L (in rounds of kCombineRound states;
 // a long sequence's rounds are shared out over the workgroup's four waves,
 // whose partial merges then meet in LDS in a fixed order), and writes the
-// zero rows of empty sequences.
+// zero rows of empty sequences. On a handle whose bounds never split a
+// sequence, the split kernel writes those zero rows itself and the step is
+// that one kernel.
 // The kernel boundary makes the split states visible across the chip's
 // separately cached dies without any in-kernel cache write-back.
 //
