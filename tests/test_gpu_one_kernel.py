@@ -126,3 +126,24 @@ def test_one_kernel_multi_token_rows():
     assert_parity(got, ref, "one-kernel multi-token")
     assert (got[ctx == 0] == 0).all()
     assert (got[7, 0] == 0).all()
+
+
+def test_one_kernel_handle_two_stage_calls_match_decode():
+    # xqa_decode_split + xqa_decode_combine stay valid on a one-kernel handle
+    # (the split kernel writes every row, the combine finds nothing to merge).
+    rng = np.random.default_rng(95)
+    ctx = rng.integers(0, 500, size=80)
+    ctx[[2, 63, 64]] = 0
+    w = make_custom(ctx.tolist(), 2, 16, [96, 0], max_pages_per_seq=32)
+    xqa = Xqa(max_batch=w.batch, num_q_heads=16, num_kv_heads=2, max_pages_per_seq=32,
+              max_work_items=2)
+    assert xqa.info["kernels_per_step"] == 1
+    dev = to_device(w)
+    args = dict(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages, block_table=dev.block_table,
+                context_lens=dev.context_lens, scale=w.scale)
+    one = xqa.decode(out=torch.full_like(dev.q, float("nan")), **args)
+    two = xqa.split(out=torch.full_like(dev.q, float("nan")), **args)
+    xqa.combine(context_lens=dev.context_lens, out=two)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    assert (one.float().cpu().numpy()[ctx == 0] == 0).all()
