@@ -18,7 +18,10 @@
 //      captured graph replays exactly with new lengths.
 //   Gather: a wave fetches the page ids of its next 32 blocks with one
 //      vector load and reads them out with v_readlane; K and V of a block are
-//      eight 16-byte loads per lane, issued one block ahead (ping-pong).
+//      eight 16-byte loads per lane, issued one block ahead (ping-pong). The
+//      stream runs on across 32-block chunks and segments: the next chunk's
+//      or segment's page ids are fetched when a chunk starts and its first
+//      block is issued as soon as a buffer frees, while the segment merges.
 //   K: lane l reads token l%16 of the page, head-dim bytes
 //      [16q, 16q+16) and [64+16q, 64+16q+16) (q = l/16): each load
 //      instruction covers 64 contiguous bytes of all 16 token rows.
@@ -480,32 +483,64 @@ struct SplitShared {
   float o[kWaves][kMaxGroup][kHeadDim + 4];
 };
 
-// One segment: blocks [jb_lo, jb_hi) of sequence b (tokens 32 jb_lo ..
-// min(n, 32 jb_hi)) for KV head h. The four waves take interleaved blocks,
-// then merge in LDS. `direct`: the segment is the whole sequence, so the
-// normalised output is written; otherwise the state goes to `rec`.
-template <int F, bool kAppend>
-__device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh, int b, int h,
-                                            int n, int jb_lo, int jb_hi, bool direct, float* rec,
-                                            int lane, int wave) {
-  const int G = a.group;
-  const int R = a.rows;
-  const int M = a.q_tokens;
-  const int Hkv = a.num_kv_heads;
-  const int t_begin = jb_lo * kBlockTokens;
-  const int t_end = min(n, jb_hi * kBlockTokens);
-  const int g = lane & 15;   // query row: token g / G, head h * G + g % G
-  const int q = lane >> 4;
-  // Query token j sits at position n - M + j and sees tokens <= n - M + j.
-  const int row_end = min(t_end, n - M + g / G + 1);
-  const int t_mask = min(t_end, n - M + 1);
+// One segment of a work item: blocks [jb_lo, jb_hi) of sequence b (n
+// tokens) for the workgroup's KV head. `direct`: the segment is the whole
+// sequence, so its rows are normalised and written to out; otherwise its
+// state goes to record `rec`.
+struct Segment {
+  int b, n, jb_lo, jb_hi;
+  bool direct;
+  float* rec;
+};
 
-  // Q^T fragments: lane (row g, quarter q) holds, for MFMA i, the eight
-  // head-dim values 64*(i/2) + 16q + 8*(i%2) + 0..7, matching the K bytes.
-  half8 qf[4];
-  if (g < R) {
-    const uint16_t* qrow = a.q + (((long long)b * M + g / G) * Hkv * G + (long long)h * G + g % G) *
-                                     kHeadDim;
+// A wave's part of a segment: its blocks are j = wave + 4m, m < my_blocks.
+// t_end: end of the segment's tokens (V rows past it are zeroed). row_end:
+// this lane's query row sees tokens < row_end (query token j sits at
+// position n - M + j and sees tokens <= n - M + j). t_mask: the smallest
+// row_end of the wave.
+struct WaveSeg {
+  int t_begin, t_end, row_end, t_mask, my_blocks, first_page, last_page;
+  const int32_t* bt;
+};
+
+__device__ __forceinline__ WaveSeg wave_seg(const AttendArgs& a, const Segment& s, int lane,
+                                            int wave) {
+  WaveSeg w;
+  const int G = a.group;
+  const int M = a.q_tokens;
+  w.t_begin = s.jb_lo * kBlockTokens;
+  w.t_end = min(s.n, s.jb_hi * kBlockTokens);
+  w.row_end = min(w.t_end, s.n - M + (lane & 15) / G + 1);
+  w.t_mask = min(w.t_end, s.n - M + 1);
+  const int nblocks = s.jb_hi - s.jb_lo;
+  w.my_blocks = nblocks > wave ? (nblocks - wave + kWaves - 1) / kWaves : 0;
+  w.first_page = w.t_begin >> 4;
+  w.last_page = (w.t_end - 1) >> 4;
+  w.bt = a.block_table + (long long)s.b * a.max_pages;
+  return w;
+}
+
+// Page ids of the wave's blocks c0 .. c0 + 31 of a segment in one vector
+// load: lane i holds page (i & 1) of block c0 + i/2 (read out later with
+// v_readlane, so address generation never waits on a scalar miss). Blocks
+// past the end read a valid page; they are masked in the tail block.
+__device__ __forceinline__ int load_ids(const WaveSeg& w, int c0, int lane, int wave) {
+  int pg = w.first_page + 2 * (wave + kWaves * (c0 + (lane >> 1))) + (lane & 1);
+  pg = min(pg, w.last_page);
+  return w.bt[pg];
+}
+
+// Q^T fragments: lane (row g, quarter q) holds, for MFMA i, the eight
+// head-dim values 64*(i/2) + 16q + 8*(i%2) + 0..7, matching the K bytes.
+__device__ __forceinline__ void load_q(const AttendArgs& a, const Segment& s, int h, int lane,
+                                       half8 (&qf)[4]) {
+  const int G = a.group;
+  const int g = lane & 15;
+  const int q = lane >> 4;
+  if (g < a.rows) {
+    const uint16_t* qrow =
+        a.q + (((long long)s.b * a.q_tokens + g / G) * a.num_kv_heads * G + (long long)h * G + g % G) *
+                  kHeadDim;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       qf[i] = *(const half8*)(qrow + 64 * (i >> 1) + 16 * q + 8 * (i & 1));
@@ -514,85 +549,28 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
 #pragma unroll
     for (int i = 0; i < 4; ++i) qf[i] = half8{0, 0, 0, 0, 0, 0, 0, 0};
   }
+}
 
-  const int koff = g * kHeadDim + 16 * q;
-  const int voff = (4 * q + (lane & 3)) * kHeadDim + 16 * ((lane >> 2) & 3);
-  const uint32_t sel1 = (lane & 2) ? 0x03020706u : 0x05040100u;
-  // E4M3 uses selh0 for the row-order byte selector of the transpose.
-  const uint32_t selh0 = F == kKvE4M3 ? ((lane & 1) ? 0x03070105u : 0x06020400u)
-                                      : ((lane & 1) ? 0x010C050Cu : 0x040C000Cu);
-  const uint32_t selh1 = (lane & 1) ? 0x030C070Cu : 0x060C020Cu;
-
-  WaveState st;
-  st.m = -INFINITY;
-  st.l = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int t = 0; t < 8; ++t) st.o[t] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  const int32_t* bt = a.block_table + (long long)b * a.max_pages;
-  const size_t page_stride = (size_t)Hkv * kPageHeadBytes;
-  const uint8_t* kbase = a.k_pages + (size_t)h * kPageHeadBytes;
-  const uint8_t* vbase = a.v_pages + (size_t)h * kPageHeadBytes;
-  const int nblocks = jb_hi - jb_lo;
-  const int my_blocks = nblocks > wave ? (nblocks - wave + kWaves - 1) / kWaves : 0;
-  const int first_page = t_begin >> 4;
-  const int last_page = (t_end - 1) >> 4;
-
-  // The wave's blocks are j = wave + 4m. Page ids are fetched 32 blocks at a
-  // time with one vector load (lane i: block m = i/2, page (i&1)) and read
-  // out with v_readlane, so address generation never waits on a scalar miss.
-  // Fused append: the new token n - 1 lies in this segment's last block
-  // unless the length was clamped to the table's capacity (then nothing is
-  // written). The wave that will read that block writes the new rows into
-  // the page first; its loads of the block then see them.
-  if constexpr (kAppend) {
-    if (t_end == n && (n < a.max_tokens || a.context_lens[b] == n) &&
-        ((n - 1 - t_begin) / kBlockTokens) % kWaves == wave) {
-      append_store(a, b, h, bt[(n - 1) / kPageSize], (n - 1) % kPageSize, lane);
-    }
+// Fused append: the new token n - 1 lies in a segment's last block unless
+// the length was clamped to the table's capacity (then nothing is written).
+// The wave that will read that block writes the new rows into the page
+// before it issues any load of the segment; its loads then see them.
+__device__ __forceinline__ void append_if_owner(const AttendArgs& a, const Segment& s,
+                                                const WaveSeg& w, int h, int lane, int wave) {
+  if (w.t_end == s.n && (s.n < a.max_tokens || a.context_lens[s.b] == s.n) &&
+      ((s.n - 1 - w.t_begin) / kBlockTokens) % kWaves == wave) {
+    append_store(a, s.b, h, w.bt[(s.n - 1) / kPageSize], (s.n - 1) % kPageSize, lane);
   }
+}
 
-  for (int c0 = 0; c0 < my_blocks; c0 += 32) {
-    int pg = first_page + 2 * (wave + kWaves * (c0 + (lane >> 1))) + (lane & 1);
-    pg = min(pg, last_page);   // blocks past the end read a valid page; masked later
-    const int ids = bt[pg];
-    const int cnt = min(32, my_blocks - c0);
-
-    auto issue = [&](RawBlock& r, int mm) {
-      const int pa = __builtin_amdgcn_readlane(ids, 2 * mm);
-      const int pb = __builtin_amdgcn_readlane(ids, 2 * mm + 1);
-      load_block(r, kbase + (size_t)pa * page_stride, kbase + (size_t)pb * page_stride,
-                 vbase + (size_t)pa * page_stride, vbase + (size_t)pb * page_stride, koff, voff);
-    };
-    auto tok0 = [&](int mm) { return t_begin + (wave + kWaves * (c0 + mm)) * kBlockTokens; };
-
-    // Two buffers in turn: while one block is processed the next is in
-    // flight. Every load in the steady-state loop is unconditional, so the
-    // compiler's waits name exactly the buffer about to be used.
-    RawBlock A, B;
-    issue(A, 0);
-    int mm = 0;
-    for (; mm + 2 < cnt; mm += 2) {
-      issue(B, mm + 1);
-      process_block<false, F>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
-                           selh0, selh1);
-      issue(A, mm + 2);
-      process_block<false, F>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, row_end, t_mask, lane,
-                           sel1, selh0, selh1);
-    }
-    if (cnt - mm == 2) {
-      issue(B, mm + 1);
-      process_block<false, F>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
-                           selh0, selh1);
-      process_block<true, F>(B, qf, st, a.scale_log2e, tok0(mm + 1), t_end, row_end, t_mask, lane,
-                          sel1, selh0, selh1);
-    } else {
-      process_block<true, F>(A, qf, st, a.scale_log2e, tok0(mm), t_end, row_end, t_mask, lane, sel1,
-                          selh0, selh1);
-    }
-  }
-
-  // Publish the wave's state.
+// The four waves' states of a segment meet in LDS (fixed order); the merged
+// (max, sum, O) is normalised and written, or stored as a split state.
+__device__ __forceinline__ void finish_segment(const AttendArgs& a, SplitShared& sh,
+                                               const Segment& s, const WaveState& st, int h,
+                                               int lane, int wave) {
+  const int R = a.rows;
+  const int g = lane & 15;
+  const int q = lane >> 4;
   if (g < R) {
     if (q == 0) {
       sh.m[wave][g] = st.m;
@@ -607,8 +585,6 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
     }
   }
   __syncthreads();
-
-  // Merge the four waves (fixed order): the segment's (max, sum, O).
   for (int e = threadIdx.x; e < R * 32; e += kThreads) {
     const int gg = e >> 5;
     const int d4 = (e & 31) * 4;
@@ -624,17 +600,17 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
       Ls += f * sh.l[w][gg];
       o += f * *(const float4v*)&sh.o[w][gg][d4];
     }
-    if (direct) {
+    if (s.direct) {
       const float inv = Ls > 0.f ? a.v_scale / Ls : 0.f;   // a row with no visible token is zero
       uint2 packed;
       packed.x = pack_half2(o[0] * inv, o[1] * inv);
       packed.y = pack_half2(o[2] * inv, o[3] * inv);
-      *(uint2*)(out_row(a, b, h, gg) + d4) = packed;
+      *(uint2*)(out_row(a, s.b, h, gg) + d4) = packed;
     } else {
-      *(float4v*)(rec + gg * kHeadDim + d4) = o;
+      *(float4v*)(s.rec + gg * kHeadDim + d4) = o;
       if (d4 == 0) {
-        rec[R * kHeadDim + gg] = M;
-        rec[R * kHeadDim + R + gg] = Ls;
+        s.rec[R * kHeadDim + gg] = M;
+        s.rec[R * kHeadDim + R + gg] = Ls;
       }
     }
   }
@@ -643,6 +619,15 @@ __device__ __forceinline__ void run_segment(const AttendArgs& a, SplitShared& sh
 
 // kAppend: the fused KV append (E5M2 only); a separate instantiation so that
 // plain decode carries none of its registers.
+//
+// A work item is a run of segments. Each wave streams its blocks through two
+// buffers (ping-pong): while one block is processed the next is in flight.
+// The stream does not stop at a chunk of 32 blocks or at a segment's end:
+// the page ids of the next chunk or segment are loaded when the current
+// chunk starts, and the first block after the chunk is issued as soon as a
+// buffer frees up, so the next segment's first K/V bytes travel while this
+// segment is merged. Every load in the steady-state loop is unconditional,
+// so the compiler's waits name exactly the buffer about to be used.
 template <int F, bool kAppend>
 __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
   __shared__ SplitShared sh;
@@ -678,21 +663,121 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
   const long long lo = item_lo(item, NB, P);
   const long long hi = item_lo(item + 1, NB, P);
 
-  SeqInfo sq = seqs.containing(lo, lane);
-  bool first = true;
-  while (true) {
+  const int g = lane & 15;
+  const int q = lane >> 4;
+  const int koff = g * kHeadDim + 16 * q;
+  const int voff = (4 * q + (lane & 3)) * kHeadDim + 16 * ((lane >> 2) & 3);
+  const uint32_t sel1 = (lane & 2) ? 0x03020706u : 0x05040100u;
+  // E4M3 uses selh0 for the row-order byte selector of the transpose.
+  const uint32_t selh0 = F == kKvE4M3 ? ((lane & 1) ? 0x03070105u : 0x06020400u)
+                                      : ((lane & 1) ? 0x010C050Cu : 0x040C000Cu);
+  const uint32_t selh1 = (lane & 1) ? 0x030C070Cu : 0x060C020Cu;
+  const size_t page_stride = (size_t)Hkv * kPageHeadBytes;
+  const uint8_t* kbase = a.k_pages + (size_t)h * kPageHeadBytes;
+  const uint8_t* vbase = a.v_pages + (size_t)h * kPageHeadBytes;
+
+  auto issue = [&](RawBlock& r, int ids, int mm) {
+    const int pa = __builtin_amdgcn_readlane(ids, 2 * mm);
+    const int pb = __builtin_amdgcn_readlane(ids, 2 * mm + 1);
+    load_block(r, kbase + (size_t)pa * page_stride, kbase + (size_t)pb * page_stride,
+               vbase + (size_t)pa * page_stride, vbase + (size_t)pb * page_stride, koff, voff);
+  };
+  // Item i's first segment keeps its state in record slot 2i, a later one
+  // (the last, when it is not whole) in slot 2i + 1.
+  auto make_segment = [&](const SeqInfo& sq, bool first) {
     const int nb = seq_blocks(sq.n);
     const long long seg_lo = lo > sq.off ? lo : sq.off;
     const long long seg_hi = hi < sq.off + nb ? hi : sq.off + nb;
-    const bool direct = item_of_block(sq.off, NB, P) == item_of_block(sq.off + nb - 1, NB, P);
-    float* rec = a.partials + ((long long)(2 * item + (first ? 0 : 1)) * Hkv + h) * a.item_stride;
-    run_segment<F, kAppend>(a, sh, sq.b, h, sq.n, (int)(seg_lo - sq.off), (int)(seg_hi - sq.off),
-                            direct, rec, lane, wave);
-    if (sq.off + nb >= hi) break;
-    first = false;
-    do {   // next non-empty sequence (one exists: this item has blocks left)
-      sq = seqs.at(sq.b + 1, lane);
-    } while (sq.n == 0);
+    Segment s;
+    s.b = sq.b;
+    s.n = sq.n;
+    s.jb_lo = (int)(seg_lo - sq.off);
+    s.jb_hi = (int)(seg_hi - sq.off);
+    s.direct = item_of_block(sq.off, NB, P) == item_of_block(sq.off + nb - 1, NB, P);
+    s.rec = a.partials + ((long long)(2 * item + (first ? 0 : 1)) * Hkv + h) * a.item_stride;
+    return s;
+  };
+
+  SeqInfo sq = seqs.containing(lo, lane);
+  Segment cur = make_segment(sq, true);
+  WaveSeg cw = wave_seg(a, cur, lane, wave);
+  if constexpr (kAppend) append_if_owner(a, cur, cw, h, lane, wave);
+  half8 qf[4];
+  load_q(a, cur, h, lane, qf);
+  RawBlock A, B;
+  int ids = 0;
+  if (cw.my_blocks > 0) {
+    ids = load_ids(cw, 0, lane, wave);
+    issue(A, ids, 0);
+  }
+
+  while (true) {
+    // The next segment of the item: the next non-empty sequence (one exists
+    // while the item has blocks left).
+    const bool has_next = sq.off + seq_blocks(sq.n) < hi;
+    SeqInfo nq = sq;
+    if (has_next) {
+      do {
+        nq = seqs.at(nq.b + 1, lane);
+      } while (nq.n == 0);
+    }
+    const Segment nxt = make_segment(nq, false);
+    const WaveSeg nw = wave_seg(a, nxt, lane, wave);
+    const bool next_blocks = has_next && nw.my_blocks > 0;
+
+    WaveState st;
+    st.m = -INFINITY;
+    st.l = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.o[t] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    // Precondition of each chunk: A holds (or is loading) its first block.
+    for (int c0 = 0; c0 < cw.my_blocks; c0 += 32) {
+      const int cnt = min(32, cw.my_blocks - c0);
+      const bool more_here = c0 + 32 < cw.my_blocks;
+      int ids_next = 0;
+      if (more_here) {
+        ids_next = load_ids(cw, c0 + 32, lane, wave);
+      } else if (next_blocks) {
+        if constexpr (kAppend) append_if_owner(a, nxt, nw, h, lane, wave);
+        ids_next = load_ids(nw, 0, lane, wave);
+      }
+      const bool follow = more_here || next_blocks;
+      auto tok0 = [&](int mm) { return cw.t_begin + (wave + kWaves * (c0 + mm)) * kBlockTokens; };
+      int mm = 0;
+      for (; mm + 2 < cnt; mm += 2) {
+        issue(B, ids, mm + 1);
+        process_block<false, F>(A, qf, st, a.scale_log2e, tok0(mm), cw.t_end, cw.row_end,
+                                cw.t_mask, lane, sel1, selh0, selh1);
+        issue(A, ids, mm + 2);
+        process_block<false, F>(B, qf, st, a.scale_log2e, tok0(mm + 1), cw.t_end, cw.row_end,
+                                cw.t_mask, lane, sel1, selh0, selh1);
+      }
+      if (cnt - mm == 2) {
+        issue(B, ids, mm + 1);
+        process_block<false, F>(A, qf, st, a.scale_log2e, tok0(mm), cw.t_end, cw.row_end,
+                                cw.t_mask, lane, sel1, selh0, selh1);
+        if (follow) issue(A, ids_next, 0);
+        process_block<true, F>(B, qf, st, a.scale_log2e, tok0(mm + 1), cw.t_end, cw.row_end,
+                               cw.t_mask, lane, sel1, selh0, selh1);
+      } else {
+        process_block<true, F>(A, qf, st, a.scale_log2e, tok0(mm), cw.t_end, cw.row_end,
+                               cw.t_mask, lane, sel1, selh0, selh1);
+        if (follow) issue(A, ids_next, 0);
+      }
+      ids = ids_next;
+    }
+    if (cw.my_blocks == 0 && next_blocks) {   // idle in this segment: start the next one now
+      if constexpr (kAppend) append_if_owner(a, nxt, nw, h, lane, wave);
+      ids = load_ids(nw, 0, lane, wave);
+      issue(A, ids, 0);
+    }
+    finish_segment(a, sh, cur, st, h, lane, wave);
+    if (!has_next) break;
+    sq = nq;
+    cur = nxt;
+    cw = nw;
+    load_q(a, cur, h, lane, qf);
   }
 }
 
