@@ -42,8 +42,8 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE x2.00, WRITE_SIZE x1.00). Valid only for the kernel sources
 # whose hash is recorded; any change to them reports null until re-measured.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "148198f03e65d3f6eba64aa735a01a768758c93c094892295d14ec065d454c66",
-    "fetch_kib": 133317.1, "fetch_scale": 2.0,
+    "sources_sha256": "529f4dd8054c7a0251370cc16e86c0b0cd8f26ce5f59999eec40515be08e93d3",
+    "fetch_kib": 133337.6, "fetch_scale": 2.0,
     "write_kib": 2323.8, "write_scale": 1.0,
 }
 
@@ -82,7 +82,8 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=0, help="oracle repetitions (0 = auto, ~10-20 s)")
     ap.add_argument("--quick", action="store_true", help="skip A/B/B/A and warm-mode extras")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the floor, multi-token, E4M3 and KV-append legs (profiling runs)")
+                    help="skip the floor, multi-token, E4M3 and KV-append legs and the clock "
+                         "readings (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (5x), the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counter readings")
@@ -169,7 +170,9 @@ def main():
     import numpy as np
     import torch
 
-    clocks_before = gpu_clocks()
+    # Profiling runs (--no-extras, --calibrate-copy) start no child process.
+    read_clocks = not (args.no_extras or args.calibrate_copy)
+    clocks_before = gpu_clocks() if read_clocks else None
     from decode_attention_paged_e5m2_amd import Xqa
     from workloads import make_config
     from workloads.device import to_device
@@ -365,29 +368,71 @@ def main():
         detail["warm_same_input_us_per_step"] = (time.perf_counter() - t) / blk * 1e6
 
     # --------------------------------------- per-launch timing of each kernel
-    # HIP events recorded on the stream the kernels are launched on: one pair
-    # around the split kernel, one around the combine kernel, per step.
+    # HIP events recorded on the stream the kernels are launched on. A spin
+    # kernel queued first keeps the GPU busy until every launch and event is
+    # queued, so the host's argument checks never sit between an event and
+    # the kernels it brackets.
+    #  - split kernel: one event pair around n_ev back-to-back launches
+    #    (variants in rotation); the mean launch duration is the pair's time
+    #    over n_ev. It includes the short gaps between consecutive kernels,
+    #    not the per-event overhead of the command processor.
+    #  - per step: one pair around the split kernel and one around the
+    #    combine kernel, for the split/combine breakdown in the details.
     n_ev = max(20, min(200, args.steps // 10))
+
+    def queued_behind_spin(enqueue):
+        spin_cycles = 20_000_000
+        for _attempt in range(6):
+            gate = torch.cuda.Event()
+            torch.cuda._sleep(spin_cycles)
+            gate.record(stream)
+            enqueue()
+            in_time = not gate.query()   # the spin outlasted the queueing
+            torch.cuda.synchronize()
+            if in_time:
+                return True
+            spin_cycles *= 4
+        return False
+
+    run_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+    def enqueue_split_run():
+        run_ev[0].record(stream)
+        for k in range(n_ev):
+            i = k % R
+            call(devs[i], outs[i], fn=xqa.split)
+        run_ev[1].record(stream)
+
+    ok_run = queued_behind_spin(enqueue_split_run)
+    split_run_ms = run_ev[0].elapsed_time(run_ev[1])
+    split_bytes = sum(kv_bytes[k % R] for k in range(n_ev))
+    split_avg_us = split_run_ms * 1e3 / n_ev
+    achieved = split_bytes / (split_run_ms * 1e-3) / 1e9
+
     ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(n_ev)]
-    for k in range(n_ev):
-        i = k % R
-        d = devs[i]
-        ev[k][0].record(stream)
-        call(d, outs[i], fn=xqa.split)
-        ev[k][1].record(stream)
-        xqa.combine(context_lens=d.context_lens, out=outs[i])
-        ev[k][2].record(stream)
-    torch.cuda.synchronize()
+
+    def enqueue_pairs():
+        for k in range(n_ev):
+            i = k % R
+            d = devs[i]
+            ev[k][0].record(stream)
+            call(d, outs[i], fn=xqa.split)
+            ev[k][1].record(stream)
+            xqa.combine(context_lens=d.context_lens, out=outs[i])
+            ev[k][2].record(stream)
+
+    ok_pairs = queued_behind_spin(enqueue_pairs)
     split_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(n_ev)]
     comb_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(n_ev)]
-    split_bytes = [kv_bytes[k % R] for k in range(n_ev)]
-    split_avg_us = statistics.mean(split_ms) * 1e3
-    achieved = sum(split_bytes) / (sum(split_ms) * 1e-3) / 1e9
+    detail["per_launch_timing_queued_behind_spin"] = ok_run and ok_pairs
     detail["split_kernel_us_mean"] = split_avg_us
-    detail["split_kernel_us_median"] = statistics.median(split_ms) * 1e3
-    detail["combine_kernel_us_mean"] = statistics.mean(comb_ms) * 1e3
+    detail["split_kernel_launches_timed"] = n_ev
+    detail["split_kernel_us_mean_event_pair_each"] = statistics.mean(split_ms) * 1e3
+    detail["split_kernel_us_median_event_pair_each"] = statistics.median(split_ms) * 1e3
+    detail["combine_kernel_us_mean_event_pair_each"] = statistics.mean(comb_ms) * 1e3
     log(f"split kernel: {split_avg_us:.2f} us mean per launch -> {achieved:.1f} GB/s "
-        f"({100 * achieved / HBM_PEAK_GBS:.1f}% of peak); combine {detail['combine_kernel_us_mean']:.2f} us")
+        f"({100 * achieved / HBM_PEAK_GBS:.1f}% of peak); combine "
+        f"{detail['combine_kernel_us_mean_event_pair_each']:.2f} us")
 
     # ------------------------------------------------- multi-token decode
     # Two new query tokens per sequence (causal between them): the G query
@@ -528,7 +573,7 @@ def main():
         log(f"KV append: {append_us:.2f} us per launch; append + decode graph {us_full:.2f} us/step; "
             f"fused {us_fused:.2f} us/step")
 
-    detail["gpu_clocks_after"] = gpu_clocks()
+    detail["gpu_clocks_after"] = gpu_clocks() if read_clocks else None
     line = {
         "metric": METRIC,
         "value": gbs,
