@@ -39,6 +39,9 @@ All arithmetic is float64 numpy. Functions:
   ties to even (the KV append's rounding)
 * ``append.append_kv``          the KV append: each sequence's new token
   encoded and written to its page slot
+* ``pages.decode_attention_pages``  attention over a selected subset of each
+  sequence's pages (``pages.kept_pages`` / ``pages.selected_tokens`` give the
+  pages and tokens a selection keeps)
 
 Pins (tests marked ``not gpu``): all 256 codes against the IEEE binary16 view
 of the code shifted into the high byte; single-token, constant-V, uniform-K,
@@ -49,6 +52,7 @@ pure-Python brute force on tiny shapes; split-and-merge equals single pass.
 from .e5m2 import decode_e5m2, E5M2_TABLE, E5M2_MAX_FINITE
 from .e4m3 import decode_e4m3, E4M3_TABLE, E4M3_MAX_FINITE
 from .append import encode_e5m2, append_kv
+from .pages import decode_attention_pages, kept_pages, selected_tokens
 from .attention import (
     decode_attention,
     decode_attention_fp8,
@@ -75,4 +79,7 @@ __all__ = [
     "E4M3_TABLE",
     "E4M3_MAX_FINITE",
     "decode_attention_fp8",
+    "decode_attention_pages",
+    "kept_pages",
+    "selected_tokens",
 ]
