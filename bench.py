@@ -17,9 +17,10 @@ consecutive steps (the headline; one-step-per-graph replays are reported too) ->
 A/B/B/A eager vs graph blocks -> per-launch HIP-event timing of the split
 kernel (the dominant one) and of the combine kernel on the stream they are
 launched on -> two query tokens per sequence (xqa_decode_multi), the same
-workload as an E4M3 cache with per-tensor scales (xqa_decode_fp8), and the
-KV append (xqa_append_kv) per launch and in a graph of append + decode
-steps, reported in detail. Prints one JSON line.
+workload as an E4M3 cache with per-tensor scales (xqa_decode_fp8), decode
+over a quarter of each sequence's pages (xqa_decode_pages), and the KV
+append (xqa_append_kv) per launch and in a graph of append + decode steps,
+reported in detail. Prints one JSON line.
 """
 
 import argparse
@@ -506,6 +507,66 @@ def main():
                                  "ratio_to_e5m2": us_e4 / us_step}
         log(f"E4M3 cache with scales: {us_e4:.2f} us/step ({us_e4 / us_step:.3f}x E5M2)")
         del graph4, devs4, out4, works4
+        torch.cuda.synchronize()
+
+        # ---------------------------------------------------- page subsets
+        # Decode over a quarter of each sequence's pages (every page drawn
+        # with probability 1/4, the last page always), through
+        # xqa_decode_pages: a selection kernel gathers the kept pages' ids,
+        # then the same split and combine kernels run over them. KV bytes
+        # count the kept tokens only.
+        from workloads import make_selection
+        xqa_p = Xqa(max_batch=w0.batch, num_q_heads=w0.num_q_heads, num_kv_heads=w0.num_kv_heads,
+                    max_pages_per_seq=w0.max_pages_per_seq, max_selected_pages=w0.max_pages_per_seq)
+        sels, kept_tokens = [], []
+        for i, w in enumerate(works):
+            sel, cnt = make_selection(w.context_lens, w.max_pages_per_seq, 0.25, [73, i])
+            tok = 0
+            for b in range(w.batch):
+                n, c = int(w.context_lens[b]), int(cnt[b])
+                if c > 0:   # ascending, in range, last page included
+                    tok += w.page_size * (c - 1) + n - w.page_size * int(sel[b, c - 1])
+            sels.append((torch.from_numpy(sel).to(dev), torch.from_numpy(cnt).to(dev)))
+            kept_tokens.append(tok)
+        outp = [torch.empty_like(d.q) for d in devs]
+
+        def call_p(i):
+            d = devs[i]
+            xqa_p.decode_pages(q=d.q, k_pages=d.k_pages, v_pages=d.v_pages, block_table=d.block_table,
+                               context_lens=d.context_lens, page_select=sels[i][0],
+                               select_counts=sels[i][1], scale=w0.scale, out=outp[i])
+
+        eager_p = []
+        for i in range(R):
+            call_p(i)
+            eager_p.append(outp[i].clone())
+        torch.cuda.synchronize()
+        graph_p = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_p):
+            for i in range(R):
+                call_p(i)
+        graph_p.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(outp[i].view(torch.int16), eager_p[i].view(torch.int16))
+                   for i in range(R)):
+            print(json.dumps({"error": "page-subset graph replay differs from eager"}))
+            return 1
+        for _ in range(max(args.warmup // R, 2)):
+            graph_p.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps // R):
+            graph_p.replay()
+        torch.cuda.synchronize()
+        us_p = (time.perf_counter() - t) / steps * 1e6
+        bytes_p = statistics.mean(kept_tokens) * w0.num_kv_heads * w0.head_dim * 2
+        detail["page_subset"] = {"pages_drawn_with_probability": 0.25,
+                                 "kept_tokens_per_step_mean": statistics.mean(kept_tokens),
+                                 "us_per_step_graph_Rstep": us_p,
+                                 "kv_gbs": bytes_p / us_p / 1e3}
+        log(f"page subset (1/4 of the pages): {us_p:.2f} us/step, {bytes_p / us_p / 1e3:.1f} GB/s KV")
+        xqa_p.close()
+        del graph_p, outp, eager_p, sels
         torch.cuda.synchronize()
 
         # ------------------------------------------------------------ KV append

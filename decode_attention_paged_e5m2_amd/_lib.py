@@ -14,7 +14,7 @@ XQA_ERR_HIP = 4
 
 EXPORTED = [
     "xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_multi",
-    "xqa_decode_fp8", "xqa_decode_append", "xqa_decode_split",
+    "xqa_decode_fp8", "xqa_decode_append", "xqa_decode_pages", "xqa_decode_split",
     "xqa_decode_combine", "xqa_append_kv", "xqa_plan", "xqa_debug_widen_e5m2",
     "xqa_debug_widen_e4m3", "xqa_status_string", "xqa_last_error",
 ]
@@ -30,6 +30,7 @@ class XqaConfig(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("max_work_items", ctypes.c_int32),
         ("max_query_tokens", ctypes.c_int32),
+        ("max_selected_pages", ctypes.c_int32),
     ]
 
 
@@ -74,6 +75,7 @@ def load() -> ctypes.CDLL:
     lib.xqa_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp]
     lib.xqa_decode_fp8.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, f32, f32, f32,
                                    vp, vp]
+    lib.xqa_decode_pages.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp]
     lib.xqa_decode_split.argtypes = dec
     lib.xqa_decode_combine.argtypes = [vp, vp, i32, vp, vp]
     lib.xqa_append_kv.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp]
@@ -86,7 +88,8 @@ def load() -> ctypes.CDLL:
     lib.xqa_last_error.argtypes = []
     lib.xqa_last_error.restype = ctypes.c_char_p
     for name in ("xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_multi",
-                 "xqa_decode_fp8", "xqa_debug_widen_e4m3", "xqa_decode_append", "xqa_decode_split",
+                 "xqa_decode_fp8", "xqa_debug_widen_e4m3", "xqa_decode_append", "xqa_decode_pages",
+                 "xqa_decode_split",
                  "xqa_decode_combine", "xqa_append_kv", "xqa_plan", "xqa_debug_widen_e5m2"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib

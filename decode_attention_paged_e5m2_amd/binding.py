@@ -46,12 +46,13 @@ class Xqa:
     def __init__(self, *, max_batch: int, num_q_heads: int, num_kv_heads: int,
                  max_pages_per_seq: int, head_dim: int = HEAD_DIM, page_size: int = PAGE_SIZE,
                  max_work_items: int = 0, max_query_tokens: int = 1,
-                 device: Optional[torch.device] = None):
+                 max_selected_pages: int = 0, device: Optional[torch.device] = None):
         lib = _lib.load()
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
             else torch.device(device)
         cfg = _lib.XqaConfig(max_batch, num_q_heads, num_kv_heads, head_dim, page_size,
-                             max_pages_per_seq, max_work_items, max_query_tokens)
+                             max_pages_per_seq, max_work_items, max_query_tokens,
+                             max_selected_pages)
         handle = ctypes.c_void_p()
         with torch.cuda.device(self.device):
             _lib.check(lib.xqa_create(ctypes.byref(cfg), ctypes.byref(handle)))
@@ -61,6 +62,7 @@ class Xqa:
         self.num_kv_heads = num_kv_heads
         self.max_pages_per_seq = max_pages_per_seq
         self.max_query_tokens = max_query_tokens
+        self.max_selected_pages = max_selected_pages
         self.head_dim = head_dim
         self.page_size = page_size
 
@@ -149,6 +151,33 @@ class Xqa:
             _lib.check(lib.xqa_decode_multi(*args[:7], M, *args[7:]))
         else:
             _lib.check(lib.xqa_decode(*args))
+        return out
+
+    def decode_pages(self, *, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                     block_table: torch.Tensor, context_lens: torch.Tensor,
+                     page_select: torch.Tensor, select_counts: torch.Tensor, scale: float,
+                     out: Optional[torch.Tensor] = None, batch: Optional[int] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """Decode over a selected subset of each sequence's pages
+        (xqa_decode_pages): page_select int32 [B, S] holds ascending logical
+        page indices, select_counts int32 [B] how many of each row to use;
+        q is [B, Hq, D]. The handle needs max_selected_pages >= S."""
+        _need(isinstance(q, torch.Tensor) and q.dim() == 3, "decode_pages() takes q [B, Hq, D]")
+        out, args = self._args(q, k_pages, v_pages, block_table, context_lens, out, batch, scale, stream)
+        batch = int(args[6])
+        for name, t in (("page_select", page_select), ("select_counts", select_counts)):
+            _need(isinstance(t, torch.Tensor) and t.dtype == torch.int32 and t.device == self.device
+                  and t.is_contiguous(), f"{name} must be contiguous int32 on {self.device}")
+        _need(page_select.dim() == 2 and page_select.shape[0] >= batch
+              and 1 <= page_select.shape[1] <= self.max_selected_pages,
+              f"page_select must be [>= batch, 1..{self.max_selected_pages}], "
+              f"got {tuple(page_select.shape)}")
+        _need(select_counts.dim() == 1 and select_counts.shape[0] >= batch,
+              "select_counts must be [>= batch]")
+        h, qp, kp, vp, btp, clp, b, sc, op, st = args
+        _lib.check(_lib.load().xqa_decode_pages(h, qp, kp, vp, btp, clp, _ptr(page_select),
+                                                _ptr(select_counts), int(page_select.shape[1]),
+                                                b, sc, op, st))
         return out
 
     def split(self, *, q, k_pages, v_pages, block_table, context_lens, scale, out=None,

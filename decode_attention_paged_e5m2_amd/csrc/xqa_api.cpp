@@ -23,6 +23,8 @@ struct xqa_handle_s {
   int combine_waves; // waves per combine workgroup
   bool direct_only;  // no sequence can leave split states: one kernel per step
   float* partials;   // workspace: grid partial records
+  int32_t* vtable;   // page-subset decode: [max_batch][max_selected_pages] page ids, then
+  int32_t* vlens;    //   [max_batch] lengths (null when max_selected_pages is 0)
   size_t workspace_bytes;
 };
 
@@ -123,8 +125,11 @@ const char* xqa_last_error(void) { return g_last_error; }
 xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
   if (!cfg || !out_handle) return fail(XQA_ERR_INVALID_ARG, "null cfg or out_handle");
   if (cfg->max_batch < 1 || cfg->num_q_heads < 1 || cfg->num_kv_heads < 1 ||
-      cfg->max_pages_per_seq < 1 || cfg->max_work_items < 0 || cfg->max_query_tokens < 0)
+      cfg->max_pages_per_seq < 1 || cfg->max_work_items < 0 || cfg->max_query_tokens < 0 ||
+      cfg->max_selected_pages < 0)
     return fail(XQA_ERR_INVALID_ARG, "sizes must be positive");
+  if (cfg->max_selected_pages > cfg->max_pages_per_seq)
+    return fail(XQA_ERR_UNSUPPORTED, "max_selected_pages above max_pages_per_seq");
   if (cfg->head_dim != xqa::kHeadDim) return fail(XQA_ERR_UNSUPPORTED, "head_dim must be 128");
   if (cfg->page_size != xqa::kPageSize) return fail(XQA_ERR_UNSUPPORTED, "page_size must be 16");
   if (cfg->num_q_heads % cfg->num_kv_heads != 0)
@@ -197,10 +202,21 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
   // split kernel, which then also writes the zero rows of empty sequences:
   // a decode step is one kernel.
   h->direct_only = max_states <= 1;
-  h->workspace_bytes = ws;
+  // Page-subset decode: a page table of max_batch rows plus their lengths.
+  const size_t vt_elems = cfg->max_selected_pages > 0
+                              ? (size_t)cfg->max_batch * cfg->max_selected_pages + cfg->max_batch
+                              : 0;
+  h->workspace_bytes = ws + vt_elems * sizeof(int32_t);
   h->partials = nullptr;
+  h->vtable = nullptr;
+  h->vlens = nullptr;
   e = hipMalloc(reinterpret_cast<void**>(&h->partials), ws);
+  if (e == hipSuccess && vt_elems > 0) {
+    e = hipMalloc(reinterpret_cast<void**>(&h->vtable), vt_elems * sizeof(int32_t));
+    if (e == hipSuccess) h->vlens = h->vtable + (size_t)cfg->max_batch * cfg->max_selected_pages;
+  }
   if (e != hipSuccess) {
+    if (h->partials) (void)hipFree(h->partials);
     delete h;
     if (e == hipErrorOutOfMemory) return fail(XQA_ERR_OUT_OF_MEMORY, "workspace allocation failed");
     return hip_fail(e, "hipMalloc");
@@ -214,6 +230,10 @@ xqa_status_t xqa_destroy(xqa_handle_t h) {
   if (!h) return XQA_OK;
   hipError_t e = hipSuccess;
   if (h->partials) e = hipFree(h->partials);
+  if (h->vtable) {
+    const hipError_t e2 = hipFree(h->vtable);
+    if (e == hipSuccess) e = e2;
+  }
   delete h;
   if (e != hipSuccess) return hip_fail(e, "hipFree");
   return XQA_OK;
@@ -357,6 +377,50 @@ xqa_status_t xqa_decode_append(xqa_handle_t h, const void* q, const void* k_new,
   a.v_new = static_cast<const uint16_t*>(v_new);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = xqa::launch_split(a, h->grid, s);
+  if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+  if (h->direct_only) return XQA_OK;
+  e = xqa::launch_combine(a, s);
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return XQA_OK;
+}
+
+xqa_status_t xqa_decode_pages(xqa_handle_t h, const void* q, const uint8_t* k_pages,
+                              const uint8_t* v_pages, const int32_t* block_table,
+                              const int32_t* context_lens, const int32_t* page_select,
+                              const int32_t* select_counts, int32_t select_stride, int32_t batch,
+                              float scale, void* out, void* stream) {
+  xqa_status_t st =
+      check_decode_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
+  if (st != XQA_OK) return st;
+  if (h->cfg.max_selected_pages == 0)
+    return fail(XQA_ERR_UNSUPPORTED, "handle created with max_selected_pages 0");
+  if (!page_select || !select_counts) return fail(XQA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned(page_select, 4) || !aligned(select_counts, 4))
+    return fail(XQA_ERR_INVALID_ARG, "page_select and select_counts must be 4-byte aligned");
+  if (select_stride < 1 || select_stride > h->cfg.max_selected_pages)
+    return fail(XQA_ERR_INVALID_ARG, "select_stride outside [1, max_selected_pages]");
+  if ((st = check_device(h)) != XQA_OK) return st;
+  xqa::SelectArgs sa;
+  sa.block_table = block_table;
+  sa.context_lens = context_lens;
+  sa.page_select = page_select;
+  sa.select_counts = select_counts;
+  sa.vtable = h->vtable;
+  sa.vlens = h->vlens;
+  sa.batch = batch;
+  sa.max_pages = h->cfg.max_pages_per_seq;
+  sa.max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
+  sa.select_stride = select_stride;
+  sa.vstride = h->cfg.max_selected_pages;
+  // The decode runs over the gathered table: its row stride and capacity
+  // are the selection's.
+  xqa::AttendArgs a = attend_args(h, q, k_pages, v_pages, h->vtable, h->vlens, batch, scale, out);
+  a.max_pages = h->cfg.max_selected_pages;
+  a.max_tokens = h->cfg.max_selected_pages * xqa::kPageSize;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = xqa::launch_select(sa, s);
+  if (e != hipSuccess) return hip_fail(e, "select kernel launch");
+  e = xqa::launch_split(a, h->grid, s);
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
   if (h->direct_only) return XQA_OK;
   e = xqa::launch_combine(a, s);

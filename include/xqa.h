@@ -79,6 +79,9 @@ typedef struct {
                              /* in workgroups, in [Hkv, Hkv*2048]                       */
   int32_t max_query_tokens;  /* 0 or 1: one query token per sequence; up to M with      */
                              /* G * M <= 16 for xqa_decode_multi                        */
+  int32_t max_selected_pages;/* 0: no page-subset decode; else the longest selection    */
+                             /* row xqa_decode_pages accepts, <= max_pages_per_seq      */
+                             /* (sizes a page table of max_batch rows in the handle)    */
 } xqa_config_t;
 
 typedef struct {
@@ -96,11 +99,12 @@ typedef struct {
 
 /* Create a handle on the current HIP device. Validates cfg, sizes the split
  * grid from the split kernel's occupancy and allocates the workspace for
- * split states (the only allocation the library makes). *out_handle is set
+ * split states and, when max_selected_pages > 0, the page-subset table (the
+ * only allocations the library makes). *out_handle is set
  * only on XQA_OK. Errors: INVALID_ARG (null pointers, non-positive sizes),
  * UNSUPPORTED (head_dim != 128, page_size != 16, Hq % Hkv != 0, G > 16,
  * G * max_query_tokens > 16, max_batch > 65536, more than 2^24 tokens per
- * sequence),
+ * sequence, max_selected_pages above max_pages_per_seq),
  * OUT_OF_MEMORY, HIP (no device). */
 xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle);
 
@@ -217,6 +221,34 @@ xqa_status_t xqa_decode_append(xqa_handle_t handle, const void* q, const void* k
                                const void* v_new, uint8_t* k_pages, uint8_t* v_pages,
                                const int32_t* block_table, const int32_t* context_lens,
                                int32_t batch, float scale, void* out, void* stream);
+
+/* Decode over a selected subset of each sequence's pages: the sparse-decode
+ * form the page "[Kernel][WIP] Follow up FlashNext batch HC fusion and QSA
+ * route audit" (section Test Result) describes, where a planner picks the KV
+ * pages each query attends over. The page does not publish the selection
+ * rule, so the selection is an input:
+ *     page_select   int32 [batch][select_stride] logical page indices of sequence b
+ *                   (index p covers tokens 16p .. 16p + 15), device memory
+ *     select_counts int32 [batch] entries of each row to use (clamped to [0, select_stride])
+ * With n as for xqa_decode, an entry p is kept iff 0 <= p < ceil(n / 16) and
+ * p is greater than every entry kept before it in its row (callers pass
+ * ascending page indices; others are skipped). The query heads of sequence b
+ * attend, exactly as in xqa_decode, over the tokens t < n of the kept pages;
+ * no kept token gives a zero row. Selecting every page in order gives
+ * xqa_decode's result bit for bit.
+ * A small kernel first gathers the kept pages' physical ids into the
+ * handle's page table (max_batch x max_selected_pages int32) with the
+ * matching lengths; the split and combine kernels of xqa_decode then run on
+ * it, so KV bytes are read only for the kept pages. E5M2 cache, one query
+ * token. Other arguments, alignment and capture rules as for xqa_decode.
+ * Errors: UNSUPPORTED when the handle was created with max_selected_pages 0;
+ * INVALID_ARG as for xqa_decode, and for null or misaligned page_select /
+ * select_counts or select_stride outside [1, max_selected_pages]; HIP. */
+xqa_status_t xqa_decode_pages(xqa_handle_t handle, const void* q, const uint8_t* k_pages,
+                              const uint8_t* v_pages, const int32_t* block_table,
+                              const int32_t* context_lens, const int32_t* page_select,
+                              const int32_t* select_counts, int32_t select_stride, int32_t batch,
+                              float scale, void* out, void* stream);
 
 /* Host mirror of the device-side plan, for diagnostics and tests:
  * context_lens_host is host memory [batch]. Each KV head's token stream

@@ -57,6 +57,7 @@ def _cfg(**over):
     (dict(max_batch=70000), 2), (dict(max_pages_per_seq=(1 << 20) + 1), 2),
     (dict(max_query_tokens=-1), 1), (dict(max_query_tokens=3), 2),
     (dict(num_q_heads=4, num_kv_heads=4, max_query_tokens=17), 2),
+    (dict(max_selected_pages=-1), 1), (dict(max_selected_pages=65), 2),
 ])
 def test_create_rejects_bad_configs_before_hip(lib, over, status):
     h = ctypes.c_void_p()
@@ -81,6 +82,7 @@ def test_null_arguments_are_rejected(lib):
                                  ctypes.c_float(0.1), null, null) == 1
     assert lib.xqa_decode_combine(null, null, 1, null, null) == 1
     assert lib.xqa_append_kv(null, null, null, null, null, 1, null, null, null) == 1
+    assert lib.xqa_decode_pages(*args[:6], null, null, 1, 1, ctypes.c_float(0.1), null, null) == 1
     assert lib.xqa_get_info(null, None) == 1
     assert lib.xqa_destroy(null) == 0
     assert lib.xqa_debug_widen_e5m2(null, null, null, 4, null) == 1

@@ -9,6 +9,7 @@ of a parity test can consume the same inputs.
 
 from .quantize import quantize_e5m2, E5M2_MAX_FINITE, POISON_CODE
 from .configs import Workload, make_config, make_custom, CONFIG_NAMES
+from .select import make_selection
 
 __all__ = [
     "quantize_e5m2",
@@ -18,4 +19,5 @@ __all__ = [
     "make_config",
     "make_custom",
     "CONFIG_NAMES",
+    "make_selection",
 ]
