@@ -172,13 +172,22 @@ __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
 
 // ---------------------------------------------------------------- the plan
 // Wave-level evaluation of the balanced plan (see xqa_internal.h). Each lane
-// reads the length of one sequence per 64-sequence chunk; prefix sums use
-// lane shuffles, so every call costs one pass over context_lens.
+// reads the length of one sequence per 64-sequence chunk and every call costs
+// one pass over context_lens.
+//
+// Inclusive prefix sum over the wave with DPP alone (no LDS round trip):
+// shifts by 1, 2, 4 and 8 lanes inside each row of 16 (lanes with no source
+// add 0) give row prefixes; then the last lane of row 0 is added to row 1 and
+// that of row 2 to row 3 (row_bcast:15), and lane 31 to rows 2 and 3
+// (row_bcast:31).
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
+  (void)lane;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
   return v;
 }
 
@@ -693,7 +702,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
     s.n = sq.n;
     s.jb_lo = (int)(seg_lo - sq.off);
     s.jb_hi = (int)(seg_hi - sq.off);
-    s.direct = item_of_block(sq.off, NB, P) == item_of_block(sq.off + nb - 1, NB, P);
+    // Items are contiguous block ranges, so the sequence lies in one item
+    // exactly when all its blocks fall in this item's range [lo, hi).
+    s.direct = sq.off >= lo && sq.off + nb <= hi;
     s.rec = a.partials + ((long long)(2 * item + (first ? 0 : 1)) * Hkv + h) * a.item_stride;
     return s;
   };
