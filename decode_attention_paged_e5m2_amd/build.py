@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_NAME = "libxqa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "xqa_kernels.hip"), os.path.join(CSRC, "xqa_api.cpp")]
+SOURCES = [os.path.join(CSRC, "xqa_kernels.hip"), os.path.join(CSRC, "xqa_select.hip"),
+           os.path.join(CSRC, "xqa_api.cpp")]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for all device code. MFMA results

@@ -13,6 +13,7 @@
 
 #include "../../include/xqa.h"
 #include "xqa_internal.h"
+#include "xqa_select.h"
 
 struct xqa_handle_s {
   xqa_config_t cfg;

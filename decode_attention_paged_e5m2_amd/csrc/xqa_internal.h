@@ -106,24 +106,7 @@ struct AppendArgs {
   int32_t max_tokens;
 };
 
-// Page-subset decode: each sequence's kept pages (see xqa_decode_pages)
-// gathered into a page table of its own, with the matching lengths.
-struct SelectArgs {
-  const int32_t* block_table;     // [batch][max_pages]
-  const int32_t* context_lens;    // [batch]
-  const int32_t* page_select;     // [batch][select_stride] logical page indices
-  const int32_t* select_counts;   // [batch]
-  int32_t* vtable;                // [batch][vstride] physical ids of the kept pages
-  int32_t* vlens;                 // [batch] tokens of the kept pages below n
-  int32_t batch;
-  int32_t max_pages;
-  int32_t max_tokens;             // max_pages * page size
-  int32_t select_stride;          // <= vstride
-  int32_t vstride;
-};
-
 hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream);
-hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_combine(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_widen(const uint8_t* in, uint16_t* out_f16, float* out_f32, int64_t n,

@@ -191,8 +191,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
 __device__ __forceinline__ long long uniform64(long long v) {
   const int lo = __builtin_amdgcn_readfirstlane((int)(v & 0xFFFFFFFFll));
   const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
@@ -226,9 +224,9 @@ __device__ SeqInfo seq_at(const int32_t* ctx, int batch, int max_tokens, int b, 
     const int incl = wave_inclusive_scan(nb, lane);
     if (b < base + 64) {
       const int src = b - base;
-      return {b, uniform(__shfl(n, src)), uniform64(prefix + __shfl(incl - nb, src))};
+      return {b, __builtin_amdgcn_readlane(n, src), prefix + __builtin_amdgcn_readlane(incl - nb, src)};
     }
-    prefix += __shfl(incl, 63);
+    prefix += __builtin_amdgcn_readlane(incl, 63);
   }
   return {b, 0, prefix};
 }
@@ -246,9 +244,9 @@ __device__ SeqInfo seq_containing(const int32_t* ctx, int batch, int max_tokens,
     const unsigned long long hit = __ballot(nb > 0 && x >= lo && x < prefix + incl);
     if (hit) {
       const int src = __ffsll((unsigned long long)hit) - 1;
-      return {base + src, uniform(__shfl(n, src)), uniform64(prefix + __shfl(incl - nb, src))};
+      return {base + src, __builtin_amdgcn_readlane(n, src), prefix + __builtin_amdgcn_readlane(incl - nb, src)};
     }
-    prefix += __shfl(incl, 63);
+    prefix += __builtin_amdgcn_readlane(incl, 63);
   }
   return {batch, 0, prefix};
 }
@@ -272,7 +270,7 @@ struct SeqTable {
       const int b_l = seq_blocks(n_l);
       const int incl = wave_inclusive_scan(b_l, lane);   // <= 64 * 2^19: no overflow
       excl_l = incl - b_l;
-      nb = uniform(__shfl(incl, 63));
+      nb = __builtin_amdgcn_readlane(incl, 63);
     } else {
       nb = plan_total_blocks(ctx, batch, max_tokens, lane);
     }
@@ -989,50 +987,6 @@ __global__ void append_kernel(AppendArgs a) {
   *(uint2*)dst = make_uint2(packed[0], packed[1]);
 }
 
-// ---------------------------------------------------------- page subsets
-// One wave per sequence gathers the physical ids of the pages its selection
-// keeps into a page table of its own and writes the matching length, so the
-// split and combine kernels then run unchanged over only those pages. An
-// entry is kept when it names a page the sequence uses and exceeds every
-// entry kept before it: with the in-range entries' running maximum taken as
-// a wave prefix scan, that is "in range and above the maximum before it". A
-// kept page's tokens sit at 16 j .. 16 j + 15 of the new table (j its rank);
-// only the last kept page can be the sequence's partial last page, so the
-// new length is 16 (kept - 1) plus what that page holds below n.
-__global__ __launch_bounds__(64) void select_kernel(SelectArgs a) {
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int n = clamp_len(a.context_lens[b], a.max_tokens);
-  const int used = (n + kPageSize - 1) / kPageSize;
-  int count = a.select_counts[b];
-  count = count < 0 ? 0 : (count > a.select_stride ? a.select_stride : count);
-  const int32_t* sel = a.page_select + (long long)b * a.select_stride;
-  const int32_t* bt = a.block_table + (long long)b * a.max_pages;
-  int32_t* vt = a.vtable + (long long)b * a.vstride;
-  int best = -1;   // largest page kept so far
-  int kept = 0;
-  for (int j0 = 0; j0 < count; j0 += 64) {
-    const int j = j0 + lane;
-    const int p = j < count ? sel[j] : -1;
-    const bool in = p >= 0 && p < used;
-    int run = in ? p : -1;   // inclusive running maximum of the in-range entries
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(run, off);
-      if (lane >= off) run = max(run, t);
-    }
-    int before = __shfl_up(run, 1);
-    before = max(lane == 0 ? -1 : before, best);
-    const bool keep = in && p > before;
-    const unsigned long long mask = __ballot(keep);
-    if (keep) vt[kept + __popcll(mask & ((1ull << lane) - 1ull))] = bt[p];
-    kept += __popcll(mask);
-    best = max(best, __shfl(run, 63));
-  }
-  if (lane == 0) {
-    a.vlens[b] = kept == 0 ? 0 : kPageSize * (kept - 1) + min(kPageSize, n - kPageSize * best);
-  }
-}
-
 // ------------------------------------------------------------ widen (test)
 // Each thread widens one group of four codes with the same helpers the K
 // path uses, so every byte position of both selectors is exercised.
@@ -1085,11 +1039,6 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const int threads = 256;
   const long long blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(select_kernel, dim3(a.batch), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,96 @@
+// Page-subset decode: per sequence, the pages a selection keeps, gathered
+// into a page table of the handle's own (see xqa_select.h).
+
+#include "xqa_select.h"
+
+namespace xqa {
+namespace {
+
+// One workgroup of 16 waves per sequence gathers the physical ids of the
+// pages its selection keeps into a page table of its own and writes the
+// matching length, so the split and combine kernels then run unchanged over
+// only those pages. An entry is kept when it names a page the sequence uses
+// and exceeds every entry kept before it, i.e. when it is in range and above
+// the maximum of the in-range entries before it. Per tile of 1024 entries
+// (one per thread, so a row's loads and its block-table gathers are one
+// memory round trip each): a DPP running maximum inside each wave, the wave
+// maxima through LDS, a ballot per wave for the kept entries and their
+// counts through LDS for the compaction. A kept page's tokens sit at
+// 16 j .. 16 j + 15 of the new table (j its rank); only the last kept page
+// can be the sequence's partial last page, so the new length is
+// 16 (kept - 1) plus what that page holds below n.
+constexpr int kSelectWaves = 16;
+constexpr int kSelectThreads = 64 * kSelectWaves;
+
+// Inclusive running maximum over the wave of values >= 0 (lanes with no
+// source contribute 0): max with the value 1, 2, 4 and 8 lanes back inside
+// each row of 16, then with the last lane of row 0 (into row 1) and of row 2
+// (into row 3), then with lane 31 (into rows 2 and 3).
+__device__ __forceinline__ int wave_inclusive_max0(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));
+  return v;
+}
+
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
+  __shared__ int s_max[kSelectWaves];
+  __shared__ int s_cnt[kSelectWaves];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = clamp_len(a.context_lens[b], a.max_tokens);
+  const int used = (n + kPageSize - 1) / kPageSize;
+  int count = a.select_counts[b];
+  count = count < 0 ? 0 : (count > a.select_stride ? a.select_stride : count);
+  const int32_t* sel = a.page_select + (long long)b * a.select_stride;
+  const int32_t* bt = a.block_table + (long long)b * a.max_pages;
+  int32_t* vt = a.vtable + (long long)b * a.vstride;
+  int best1 = 0;   // 1 + the largest page kept so far (0: none yet)
+  int kept = 0;
+  for (int j0 = 0; j0 < count; j0 += kSelectThreads) {
+    const int j = j0 + tid;
+    const int p = j < count ? sel[j] : -1;
+    const bool in = p >= 0 && p < used;
+    const int run = wave_inclusive_max0(in ? p + 1 : 0);
+    if (lane == 63) s_max[wave] = run;
+    __syncthreads();
+    int before = best1;
+    for (int w = 0; w < wave; ++w) before = max(before, s_max[w]);
+    const int prev = __shfl_up(run, 1);
+    if (lane > 0) before = max(before, prev);
+    const bool keep = in && p + 1 > before;
+    const unsigned long long mask = __ballot(keep);
+    if (lane == 0) s_cnt[wave] = __popcll(mask);
+    __syncthreads();
+    int off = kept;
+    int total = 0;
+    int tile_max = best1;
+    for (int w = 0; w < kSelectWaves; ++w) {
+      const int c = s_cnt[w];
+      total += c;
+      off += w < wave ? c : 0;
+      tile_max = max(tile_max, s_max[w]);
+    }
+    if (keep) vt[off + __popcll(mask & ((1ull << lane) - 1ull))] = bt[p];
+    kept += total;
+    best1 = tile_max;
+    __syncthreads();   // s_max and s_cnt are rewritten by the next tile
+  }
+  if (tid == 0) {
+    a.vlens[b] = kept == 0 ? 0 : kPageSize * (kept - 1) + min(kPageSize, n - kPageSize * (best1 - 1));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(select_kernel, dim3(a.batch), dim3(kSelectThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace xqa
