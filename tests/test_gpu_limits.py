@@ -1,5 +1,6 @@
 """GPU tests at the documented maximum sizes: a sequence of 2^24 tokens
-(max_pages_per_seq * 16) and a batch of 65536 sequences.
+(max_pages_per_seq * 16), also through page-subset decode with a selection
+row of 2^20 pages, and a batch of 65536 sequences.
 
 The longest sequence is checked through a closed form instead of the
 element-wise oracle: with every K row the same code all scores are equal,
@@ -71,6 +72,42 @@ def test_longest_sequence_2_pow_24_tokens():
         # fp16 output rounding of values in [1, 2] is at most 2^-11; the fp32
         # sums over up to 2^24 tokens add far less than 1e-4.
         assert err <= 2.0 ** -11 + 1e-4
+    xqa.close()
+
+    # Page-subset decode over the same sequence: a selection row of 2^20
+    # pages (1024 tiles of the selection kernel). Every page in order is
+    # plain decode bit for bit; every third page plus the partial last one
+    # is the mean of the pattern over the tokens those pages hold.
+    xqa_p = Xqa(max_batch=1, num_q_heads=hq, num_kv_heads=hkv, max_pages_per_seq=pages,
+                max_selected_pages=pages)
+    length = n - 5
+    lens = torch.tensor([length], dtype=torch.int32, device=dev)
+    every = torch.arange(pages, dtype=torch.int32, device=dev).view(1, pages)
+    plain = xqa_p.decode(q=q, k_pages=k, v_pages=v, block_table=bt, context_lens=lens, scale=0.088)
+    sub = xqa_p.decode_pages(q=q, k_pages=k, v_pages=v, block_table=bt, context_lens=lens,
+                             page_select=every,
+                             select_counts=torch.tensor([pages], dtype=torch.int32, device=dev),
+                             scale=0.088)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), sub.view(torch.int16))
+    chosen = np.append(np.arange(0, pages - 1, 3), pages - 1)
+    row = torch.full((1, pages), -1, dtype=torch.int32, device=dev)
+    row[0, :chosen.size] = torch.from_numpy(chosen.astype(np.int32)).to(dev)
+    sub = xqa_p.decode_pages(q=q, k_pages=k, v_pages=v, block_table=bt, context_lens=lens,
+                             page_select=row,
+                             select_counts=torch.tensor([chosen.size], dtype=torch.int32, device=dev),
+                             scale=0.088)
+    torch.cuda.synchronize()
+    toks = (16 * chosen[:, None] + np.arange(16)[None, :]).ravel()
+    toks = toks[toks < length]
+    hist = np.bincount(toks % 5, minlength=5)            # tokens with t % 5 == r
+    vals = E5M2_TABLE[CODES]
+    want = np.array([(hist * vals[(np.arange(5) + dd) % 5]).sum() / toks.size for dd in range(128)])
+    err = np.abs(sub.float().cpu().numpy()[0] - want[None, :]).max()
+    print(f"[limits] page subset: {chosen.size} of {pages} pages, {toks.size} tokens, "
+          f"max|err|={err:.2e}", flush=True)
+    assert err <= 2.0 ** -11 + 1e-4
+    xqa_p.close()
 
 
 def test_largest_batch_65536_sequences():
