@@ -175,7 +175,7 @@ def make_config(index: int, variant: int = 0, with_tokens: bool = True,
     """
     seed = [1000 + index, variant]
     rng = np.random.default_rng(seed)
-    name = f"cfg{index}_{CONFIG_NAMES[index]}_v{variant}"
+    name = f"{CONFIG_NAMES[index]}_v{variant}"
     kw = dict(name=name, rng=rng, with_tokens=with_tokens, kv_format=kv_format)
     if index == 1:
         return make_custom([256], 1, 8, seed, pool_pages=16, max_pages_per_seq=16,
