@@ -48,7 +48,7 @@ def test_config_shapes():
         w = make_config(idx, with_tokens=False)
         assert (w.batch, w.num_kv_heads, w.num_q_heads, w.max_pages_per_seq, w.num_pages) == \
             (B, hkv, hq, mp, npg), idx
-        assert w.name.startswith(f"cfg{idx}_") and CONFIG_NAMES[idx] in w.name
+        assert w.name == f"{CONFIG_NAMES[idx]}_v0"
         check_block_table(w)
     assert make_config(1, with_tokens=False).context_lens.tolist() == [256]
     assert (make_config(1, with_tokens=False).block_table[0] == np.arange(16)).all()
