@@ -16,7 +16,8 @@ independent warm-up of each arm -> timed replays of one graph holding R
 consecutive steps (the headline; one-step-per-graph replays are reported too) ->
 A/B/B/A eager vs graph blocks -> per-launch HIP-event timing of the split
 kernel (the dominant one) and of the combine kernel on the stream they are
-launched on -> two query tokens per sequence (xqa_decode_multi), the same
+launched on -> single steps timed cold (caches flushed by reading 1 GiB
+before each) and warm (the same input repeated) -> two query tokens per sequence (xqa_decode_multi), the same
 workload as an E4M3 cache with per-tensor scales (xqa_decode_fp8), decode
 over a quarter of each sequence's pages (xqa_decode_pages), and the KV
 append (xqa_append_kv) per launch and in a graph of append + decode steps,
@@ -434,6 +435,45 @@ def main():
     log(f"split kernel: {split_avg_us:.2f} us mean per launch -> {achieved:.1f} GB/s "
         f"({100 * achieved / HBM_PEAK_GBS:.1f}% of peak); combine "
         f"{detail['combine_kernel_us_mean_event_pair_each']:.2f} us")
+
+    # ------------------------------------------------- cold vs warm steps
+    # One decode step per graph replay, bracketed by its own HIP event pair.
+    # Cold: before each step a reduction reads a 1 GiB buffer (untimed,
+    # outside the pair; it writes one byte, so no dirty lines are left to
+    # write back), which streams through the L2 caches and the 256 MiB
+    # on-package cache: the step reads its KV bytes from HBM even when they
+    # would fit on package.
+    # Warm: the same variant's step repeated with nothing in between. Both
+    # carry the same event-pair overhead (~2 us), so their difference is the
+    # cache effect alone.
+    if not args.quick:
+        flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        flush_out = torch.empty((), dtype=torch.uint8, device=dev)
+        n_cold = max(20, min(100, args.steps // 20))
+
+        def event_steps(flush):
+            pairs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+                     for _ in range(n_cold)]
+
+            def enqueue():
+                for k in range(n_cold):
+                    if flush:
+                        torch.amax(flush_buf, dim=0, out=flush_out)
+                    pairs[k][0].record(stream)
+                    graphs[k % R if flush else 0].replay()
+                    pairs[k][1].record(stream)
+
+            ok = queued_behind_spin(enqueue)
+            return ok, statistics.median(a.elapsed_time(b) * 1e3 for a, b in pairs)
+
+        ok_c, cold_us = event_steps(True)
+        ok_w, warm_us = event_steps(False)
+        detail["cold_vs_warm_event_pair_us_per_step"] = {
+            "cold_flushed_median": cold_us, "warm_same_input_median": warm_us,
+            "steps": n_cold, "queued_behind_spin": ok_c and ok_w}
+        log(f"one step per event pair: cold (1 GiB read before each) {cold_us:.2f} us, "
+            f"warm (same input repeated) {warm_us:.2f} us")
+        del flush_buf, flush_out
 
     # ------------------------------------------------- multi-token decode
     # Two new query tokens per sequence (causal between them): the G query
