@@ -17,10 +17,12 @@ ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for all device code. MFMA results
 # are kept in ordinary VGPRs (no AGPR copies around the softmax arithmetic).
+# The first four dwords of kernel arguments are preloaded into SGPRs at wave
+# launch (the attention kernels put the plan's inputs there).
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    "-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=4",
     "-I", INCLUDE,
 ]
 

@@ -635,14 +635,21 @@ __device__ __forceinline__ void finish_segment(const AttendArgs& a, SplitShared&
 // buffer frees up, so the next segment's first K/V bytes travel while this
 // segment is merged. Every load in the steady-state loop is unconditional,
 // so the compiler's waits name exactly the buffer about to be used.
+//
+// This kernel and the combine kernel take the three values the plan needs
+// first (context_lens, batch, max_tokens) as leading scalar arguments ahead
+// of the argument block: the build preloads them into SGPRs
+// (amdgpu-kernarg-preload-count=4), so the first load of context_lens is
+// issued without waiting for the argument block to arrive from memory.
 template <int F, bool kAppend>
-__global__ __launch_bounds__(kThreads) void split_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_lens, int32_t batch,
+                                                         int32_t max_tokens, AttendArgs a) {
   __shared__ SplitShared sh;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int Hkv = a.num_kv_heads;
 
-  const SeqTable seqs(a.context_lens, a.batch, a.max_tokens, lane);
+  const SeqTable seqs(context_lens, batch, max_tokens, lane);
   const long long NB = seqs.nb;
   const int P = items_per_head(NB, a.per_head);
   const int item = blockIdx.x / Hkv;
@@ -839,7 +846,8 @@ struct CombineShared {
 };
 
 template <int W>
-__global__ __launch_bounds__(64 * W) void combine_kernel(AttendArgs a) {
+__global__ __launch_bounds__(64 * W) void combine_kernel(const int32_t* context_lens, int32_t batch,
+                                                         int32_t max_tokens, AttendArgs a) {
   constexpr int kWgCols = 16 * W;
   constexpr int kChunks = kHeadDim / kWgCols;
   const int lane = threadIdx.x & 63;
@@ -851,7 +859,7 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(AttendArgs a) {
   const int b = bh / Hkv;
   const int h = bh % Hkv;
 
-  const SeqTable seqs(a.context_lens, a.batch, a.max_tokens, lane);
+  const SeqTable seqs(context_lens, batch, max_tokens, lane);
   const long long NB = seqs.nb;
   const int P = items_per_head(NB, a.per_head);
   const SeqInfo sq = seqs.at(b, lane);
@@ -1013,11 +1021,14 @@ __global__ void widen_kernel(const uint8_t* in, uint16_t* out16, float* out32, l
 
 hipError_t launch_split(const AttendArgs& a, int grid, hipStream_t stream) {
   if (a.k_new != nullptr) {
-    hipLaunchKernelGGL((split_kernel<kKvE5M2, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((split_kernel<kKvE5M2, true>), dim3(grid), dim3(kThreads), 0, stream,
+                       a.context_lens, a.batch, a.max_tokens, a);
   } else if (a.kv_format == kKvE4M3) {
-    hipLaunchKernelGGL((split_kernel<kKvE4M3, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((split_kernel<kKvE4M3, false>), dim3(grid), dim3(kThreads), 0, stream,
+                       a.context_lens, a.batch, a.max_tokens, a);
   } else {
-    hipLaunchKernelGGL((split_kernel<kKvE5M2, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((split_kernel<kKvE5M2, false>), dim3(grid), dim3(kThreads), 0, stream,
+                       a.context_lens, a.batch, a.max_tokens, a);
   }
   return hipGetLastError();
 }
@@ -1026,10 +1037,12 @@ hipError_t launch_combine(const AttendArgs& a, hipStream_t stream) {
   if (a.combine_waves == kCombineMaxWaves) {
     constexpr int W = kCombineMaxWaves;
     const int grid = a.batch * a.num_kv_heads * (kHeadDim / (16 * W));
-    hipLaunchKernelGGL(combine_kernel<W>, dim3(grid), dim3(64 * W), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<W>, dim3(grid), dim3(64 * W), 0, stream, a.context_lens,
+                       a.batch, a.max_tokens, a);
   } else {
     const int grid = a.batch * a.num_kv_heads * (kHeadDim / 16);
-    hipLaunchKernelGGL(combine_kernel<1>, dim3(grid), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<1>, dim3(grid), dim3(64), 0, stream, a.context_lens,
+                       a.batch, a.max_tokens, a);
   }
   return hipGetLastError();
 }
