@@ -561,7 +561,7 @@ __device__ __forceinline__ void load_q(const AttendArgs& a, const Segment& s, in
 // Fused append: the new token n - 1 lies in a segment's last block unless
 // the length was clamped to the table's capacity (then nothing is written).
 // The wave that will read that block writes the new rows into the page
-// before it issues any load of the segment; its loads then see them.
+// before it issues any K/V load of the segment; its loads then see them.
 __device__ __forceinline__ void append_if_owner(const AttendArgs& a, const Segment& s,
                                                 const WaveSeg& w, int h, int lane, int wave) {
   if (w.t_end == s.n && (s.n < a.max_tokens || a.context_lens[s.b] == s.n) &&
@@ -717,15 +717,15 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
   SeqInfo sq = seqs.containing(lo, lane);
   Segment cur = make_segment(sq, true);
   WaveSeg cw = wave_seg(a, cur, lane, wave);
-  if constexpr (kAppend) append_if_owner(a, cur, cw, h, lane, wave);
   half8 qf[4];
   load_q(a, cur, h, lane, qf);
   RawBlock A, B;
   int ids = 0;
-  if (cw.my_blocks > 0) {
-    ids = load_ids(cw, 0, lane, wave);
-    issue(A, ids, 0);
-  }
+  if (cw.my_blocks > 0) ids = load_ids(cw, 0, lane, wave);
+  // The append's loads travel with the page-id and Q loads; its store still
+  // precedes every K/V load of the segment.
+  if constexpr (kAppend) append_if_owner(a, cur, cw, h, lane, wave);
+  if (cw.my_blocks > 0) issue(A, ids, 0);
 
   while (true) {
     // The next segment of the item: the next non-empty sequence (one exists
@@ -755,8 +755,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
       if (more_here) {
         ids_next = load_ids(cw, c0 + 32, lane, wave);
       } else if (next_blocks) {
-        if constexpr (kAppend) append_if_owner(a, nxt, nw, h, lane, wave);
         ids_next = load_ids(nw, 0, lane, wave);
+        if constexpr (kAppend) append_if_owner(a, nxt, nw, h, lane, wave);
       }
       const bool follow = more_here || next_blocks;
       auto tok0 = [&](int mm) { return cw.t_begin + (wave + kWaves * (c0 + mm)) * kBlockTokens; };
@@ -784,8 +784,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
       ids = ids_next;
     }
     if (cw.my_blocks == 0 && next_blocks) {   // idle in this segment: start the next one now
-      if constexpr (kAppend) append_if_owner(a, nxt, nw, h, lane, wave);
       ids = load_ids(nw, 0, lane, wave);
+      if constexpr (kAppend) append_if_owner(a, nxt, nw, h, lane, wave);
       issue(A, ids, 0);
     }
     finish_segment(a, sh, cur, st, h, lane, wave);
