@@ -218,7 +218,7 @@ def test_scale_zero_gives_mean_of_v():
 def test_repeat_stages_and_permutation_bitwise():
     w = make_custom([3000, 17, 700, 4096, 1], 4, 32, 47, pool_pages=800)
     out, xqa, dev = run(w)
-    for _ in range(20):
+    for _ in range(100):
         again, _, _ = run(w, xqa=xqa, dev=dev)
         assert (again.view(np.uint32) == out.view(np.uint32)).all()
     # split + combine called separately == decode, bitwise
@@ -227,7 +227,7 @@ def test_repeat_stages_and_permutation_bitwise():
               context_lens=dev.context_lens, scale=w.scale, out=o2)
     xqa.combine(context_lens=dev.context_lens, out=o2)
     torch.cuda.synchronize()
-    assert (o2.float().cpu().numpy() == out).all()
+    assert (o2.float().cpu().numpy().view(np.uint32) == out.view(np.uint32)).all()
     # moving every page to another physical slot leaves the result bitwise equal
     perm = torch.randperm(dev.k_pages.shape[0], generator=torch.Generator().manual_seed(3)).cuda()
     k2 = torch.empty_like(dev.k_pages)
@@ -236,7 +236,7 @@ def test_repeat_stages_and_permutation_bitwise():
     v2[perm] = dev.v_pages
     bt2 = perm[dev.block_table.long()].to(torch.int32)
     o3, _, _ = run(w, xqa=xqa, dev=dev, k_pages=k2, v_pages=v2, block_table=bt2)
-    assert (o3 == out).all()
+    assert (o3.view(np.uint32) == out.view(np.uint32)).all()
 
 
 def test_alternating_inputs_never_read_stale_split_states():
