@@ -347,6 +347,24 @@ def main():
         log(f"floor (all lengths 0, same graph shape): {us_floor:.2f} us/step")
         detail["floor_us_per_step_zero_lengths"] = us_floor
         del floor_g
+        # Launch floor: a graph of as many empty kernels (a zero-cycle spin)
+        # as the decode graph has launches, replayed the same way.
+        kernels_per_step = int(info.get("kernels_per_step", 2))
+        empty_g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(empty_g):
+            for _ in range(R * kernels_per_step):
+                torch.cuda._sleep(0)
+        for _ in range(max(args.warmup // R, 2)):
+            empty_g.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps // R):
+            empty_g.replay()
+        torch.cuda.synchronize()
+        us_empty = (time.perf_counter() - t) / steps * 1e6
+        log(f"launch floor ({kernels_per_step} empty kernels per step): {us_empty:.2f} us/step")
+        detail["floor_us_per_step_empty_kernels"] = us_empty
+        del empty_g
 
     # ------------------------------------------------------ A/B/B/A blocks
     if not args.quick:
