@@ -17,7 +17,9 @@ constexpr int kMinItemBlocks = 8;                      // smallest work item: 8 
 constexpr int kMaxItemsPerHead = 2048;                 // bound on work items per KV head
 constexpr int kMaxSeqTokens = 1 << 24;                 // bound on max_pages_per_seq * page_size
 constexpr int kMaxBatch = 1 << 16;                     // bound on max_batch
-constexpr int kCombineRound = 16;                      // split states loaded per round
+constexpr int kCombineRound = 16;                      // split states per round, one wave per round
+constexpr int kCombineSharedRound = 8;                 // per round when a sequence's rounds are shared
+                                                       // over the waves of a workgroup
 constexpr int kCombineMaxWaves = 4;                    // waves per combine workgroup (1 or 4)
 
 // ---------------------------------------------------------------------------

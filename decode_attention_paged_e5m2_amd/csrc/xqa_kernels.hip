@@ -54,8 +54,8 @@
 //
 // The combine kernel then merges the states of every split sequence with
 // the exact log-sum-exp rule M = max m_s, L = sum l_s 2^(m_s-M),
-// out = v_scale * sum 2^(m_s-M) O_s / L (in rounds of kCombineRound states;
-// a long sequence's rounds are shared out over the workgroup's four waves,
+// out = v_scale * sum 2^(m_s-M) O_s / L (in rounds of loaded states; a long
+// sequence's rounds are shared out over the workgroup's four waves,
 // whose partial merges then meet in LDS in a fixed order), and writes the
 // zero rows of empty sequences. On a handle whose bounds never split a
 // sequence, the split kernel writes those zero rows itself and the step is
@@ -809,29 +809,30 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
 // round trip per round and no cross-lane step.
 //
 // More states with W = 4 (a long sequence split over many items): the four
-// waves split the rounds (wave w takes rounds w, w+4, ...), lane t owning 8
-// columns of row t/8 across the workgroup's 64; the four partial merges then
-// meet in LDS in wave order. The split depends on the state count only, so
-// the result is the same on every run.
+// waves split rounds of kCombineSharedRound states (wave w takes rounds w,
+// w+4, ...), lane t owning 8 columns of row t/8 across the workgroup's 64;
+// the four partial merges then meet in LDS in wave order. The split depends
+// on the state count only, so the result is the same on every run. Rounds
+// of 8 rather than 16 here keep the kernel at ~100 VGPRs instead of ~155,
+// which measured faster for both paths.
 
 // Merges one round of split states (cnt valid entries) into (M, L, o[0..N)).
 // A state of a query row that saw no token has m = -inf and weight 0; equal
 // maxima keep the sums unscaled.
-template <int N>
-__device__ __forceinline__ void merge_round(const float (&mv)[kCombineRound],
-                                            const float (&lv)[kCombineRound],
-                                            const float (&ov)[kCombineRound][N], int cnt,
-                                            float& M, float& L, float (&o)[N]) {
+template <int K, int N>
+__device__ __forceinline__ void merge_round(const float (&mv)[K], const float (&lv)[K],
+                                            const float (&ov)[K][N], int cnt, float& M, float& L,
+                                            float (&o)[N]) {
   float mr = M;
 #pragma unroll
-  for (int k = 0; k < kCombineRound; ++k) mr = fmaxf(mr, k < cnt ? mv[k] : -INFINITY);
+  for (int k = 0; k < K; ++k) mr = fmaxf(mr, k < cnt ? mv[k] : -INFINITY);
   const float fa = M == mr ? 1.f : exp2_fast(M - mr);   // 0 on the first round
   L *= fa;
 #pragma unroll
   for (int c = 0; c < N; ++c) o[c] *= fa;
   M = mr;
 #pragma unroll
-  for (int k = 0; k < kCombineRound; ++k) {
+  for (int k = 0; k < K; ++k) {
     const float w = (k < cnt && mv[k] != -INFINITY) ? exp2_fast(mv[k] - M) : 0.f;
     L += w * lv[k];
 #pragma unroll
@@ -900,7 +901,7 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int32_t* context_
         lv[k] = r[mo + R + gg];
       }
       float M = -INFINITY, L = 0.f, o[2] = {0.f, 0.f};
-      merge_round<2>(mv, lv, ov, min(nsb, kCombineRound), M, L, o);
+      merge_round<kCombineRound, 2>(mv, lv, ov, min(nsb, kCombineRound), M, L, o);
       const float inv = L > 0.f ? a.v_scale / L : 0.f;   // a row with no visible token is zero
       *(uint32_t*)(out_row(a, b, h, gg) + c) = pack_half2(o[0] * inv, o[1] * inv);
     }
@@ -916,10 +917,10 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int32_t* context_
       const int c = chunk * kWgCols + (e & 7) * 8;
       float M = -INFINITY, L = 0.f;
       float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int s0 = kCombineRound * wave; s0 < nsb; s0 += kCombineRound * W) {
-        float mv[kCombineRound], lv[kCombineRound], ov[kCombineRound][8];
+      for (int s0 = kCombineSharedRound * wave; s0 < nsb; s0 += kCombineSharedRound * W) {
+        float mv[kCombineSharedRound], lv[kCombineSharedRound], ov[kCombineSharedRound][8];
 #pragma unroll
-        for (int k = 0; k < kCombineRound; ++k) {
+        for (int k = 0; k < kCombineSharedRound; ++k) {
           const float* r = rec(min(s0 + k, nsb - 1));
           const float4v v0 = *(const float4v*)(r + gg * kHeadDim + c);
           const float4v v1 = *(const float4v*)(r + gg * kHeadDim + c + 4);
@@ -931,7 +932,8 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int32_t* context_
           mv[k] = r[mo + gg];
           lv[k] = r[mo + R + gg];
         }
-        merge_round<8>(mv, lv, ov, min(kCombineRound, nsb - s0), M, L, o);
+        merge_round<kCombineSharedRound, 8>(mv, lv, ov, min(kCombineSharedRound, nsb - s0), M, L,
+                                            o);
       }
       sh.m[wave][e] = M;   // -inf and 0 for a wave with no rounds
       sh.l[wave][e] = L;
