@@ -15,7 +15,7 @@ import torch
 import oracle
 from oracle.e5m2 import E5M2_TABLE
 from tests._helpers import assert_parity, ensure_library
-from workloads import make_custom
+from workloads import make_custom, make_selection
 from workloads.device import to_device
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -127,3 +127,18 @@ def test_largest_batch_65536_sequences():
     got = out.float().cpu().numpy()
     assert_parity(got, ref, "batch 65536")
     assert (got[lens == 0] == 0).all()
+    xqa.close()
+
+    # Page-subset decode over the same batch: 65536 selection workgroups.
+    sel, counts = make_selection(lens.tolist(), w.max_pages_per_seq, 0.5, [83], messy=True)
+    xqa = Xqa(max_batch=B, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=w.max_pages_per_seq,
+              max_selected_pages=w.max_pages_per_seq)
+    out = xqa.decode_pages(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages,
+                           block_table=dev.block_table, context_lens=dev.context_lens,
+                           page_select=torch.from_numpy(sel).cuda(),
+                           select_counts=torch.from_numpy(counts).cuda(), scale=w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention_pages(w.q, kp, vp, w.block_table, w.context_lens, sel, counts,
+                                        w.scale)
+    assert_parity(out.float().cpu().numpy(), ref, "batch 65536, page subsets")
+    xqa.close()
