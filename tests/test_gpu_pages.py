@@ -70,6 +70,21 @@ def test_ragged_messy_selection_vs_oracle(hkv, hq):
     xqa.close()
 
 
+@pytest.mark.parametrize("items_per_head", [1, 2, 5])
+def test_few_work_items_span_sequences(items_per_head):
+    # Few items per KV head: items run many segments of the gathered table,
+    # and long selections leave states in several items.
+    lens = [5000, 17, 0, 2047, 1, 3000, 640, 33]
+    w = make_custom(lens, 2, 16, [78, items_per_head], pool_pages=700)
+    sel, counts = make_selection(lens, w.max_pages_per_seq, 0.6, [79, items_per_head], messy=True)
+    xqa = handle_for(w, max_work_items=2 * items_per_head)
+    d = to_device(w)
+    got = run_pages(xqa, w, d, sel, counts).float().cpu().numpy()
+    st = assert_parity(got, reference(w, sel, counts), f"items/head {items_per_head}")
+    log(f"items/head {items_per_head}", st)
+    xqa.close()
+
+
 def test_every_page_in_order_is_decode_bit_for_bit():
     w = make_config(4)
     d = to_device(w)
