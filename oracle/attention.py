@@ -45,6 +45,11 @@ def gather_tokens(pages: np.ndarray, block_table: np.ndarray, b: int, h: int, n:
     return E5M2_TABLE[codes]
 
 
+def _kv_head(hq: int, Hq: int, Hkv: int) -> int:
+    """KV head read by query head hq: contiguous groups of G = Hq / Hkv (a reading)."""
+    return hq // (Hq // Hkv)
+
+
 def _effective_len(context_lens, block_table, P, b) -> int:
     n = int(context_lens[b])
     return max(0, min(n, block_table.shape[1] * P))
@@ -56,8 +61,7 @@ def decode_attention_row(q, k_pages, v_pages, block_table, context_lens, scale, 
     Hkv = k_pages.shape[1]
     P = k_pages.shape[2]
     D = k_pages.shape[3]
-    G = Hq // Hkv
-    h = hq // G
+    h = _kv_head(hq, Hq, Hkv)
     n = _effective_len(context_lens, block_table, P, b)
     if n == 0:
         return np.zeros(D, dtype=np.float64)

@@ -257,3 +257,107 @@ def test_brute_force_catches_planted_mistakes(monkeypatch, which):
     _planted(monkeypatch, which)
     out = run_oracle(w)
     assert not np.allclose(out, ref, rtol=1e-6, equal_nan=True)
+
+
+# ------------------------------- the row and split-state forms, on their own
+# decode_attention_row and partial_state are pinned here against the
+# pure-Python brute force (its own head map, gather and math.exp / math.fsum
+# sums) at several KV heads and at group sizes 1 and 8, so a wrong head map or
+# scale in either one fails; their agreement with each other is not used.
+
+def brute_force_state(w, b, hq):
+    """(m, l, o) of row (b, hq) over all its tokens with explicit loops."""
+    G = w.num_q_heads // w.num_kv_heads
+    h = hq // G
+    n = max(0, min(int(w.context_lens[b]), w.max_pages_per_seq * w.page_size))
+    kp, vp = w.pools()
+    s = float(np.float32(w.scale))
+    qv = [float(x) for x in w.q[b, hq, :]]
+    z, vrows = [], []
+    for t in range(n):
+        page = int(w.block_table[b][t // w.page_size])
+        slot = t % w.page_size
+        kt = [_dec_bytes(int(c)) for c in kp[page, h, slot, :]]
+        vrows.append([_dec_bytes(int(c)) for c in vp[page, h, slot, :]])
+        z.append(s * math.fsum(qv[d] * kt[d] for d in range(w.head_dim)))
+    m = max(z)
+    e = [math.exp(zt - m) for zt in z]
+    o = [math.fsum(e[t] * vrows[t][d] for t in range(n)) for d in range(w.head_dim)]
+    return m, math.fsum(e), np.array(o)
+
+
+ROW_SHAPES = [  # (context lengths, Hkv, Hq): group sizes 8 and 1, two and four KV heads
+    ([23, 40], 2, 16),
+    ([37, 1], 4, 4),
+    ([18], 2, 2),
+]
+
+
+def _row_close(got, ref):
+    scale = max(np.abs(ref).max(), 1e-300)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12 * scale)
+
+
+@pytest.mark.parametrize("ctx,hkv,hq", ROW_SHAPES)
+def test_decode_attention_row_matches_brute_force(ctx, hkv, hq):
+    w = make_custom(ctx, hkv, hq, 40 + hq, pool_pages=sum((c + 15) // 16 for c in ctx) + 2)
+    kp, vp = w.pools()
+    full = run_oracle(w)
+    for b in range(w.batch):
+        for h in range(hq):
+            row = oracle.decode_attention_row(w.q, kp, vp, w.block_table, w.context_lens,
+                                              w.scale, b, h)
+            ref = np.array(brute_force(w, b, h))
+            _row_close(row, ref)
+            _row_close(full[b, h], ref)
+
+
+@pytest.mark.parametrize("ctx,hkv,hq", ROW_SHAPES)
+def test_partial_state_over_all_tokens_matches_brute_force(ctx, hkv, hq):
+    w = make_custom(ctx, hkv, hq, 50 + hq, pool_pages=sum((c + 15) // 16 for c in ctx) + 2)
+    kp, vp = w.pools()
+    G = hq // hkv
+    for b in range(w.batch):
+        n = int(w.context_lens[b])
+        for h in range(hq):
+            # The test gathers with its own head map (contiguous groups).
+            K = A.gather_tokens(kp, w.block_table, b, h // G, n)
+            V = A.gather_tokens(vp, w.block_table, b, h // G, n)
+            m, l, o = oracle.partial_state(w.q[b, h], K, V, w.scale)
+            bm, bl, bo = brute_force_state(w, b, h)
+            assert abs(m - bm) <= 1e-12 * max(abs(bm), 1.0)
+            assert abs(l - bl) <= 1e-12 * bl
+            _row_close(o, bo)
+            _row_close(oracle.merge_states([(m, l, o)]), np.array(brute_force(w, b, h)))
+
+
+def _plant_row_state(monkeypatch, which):
+    if which == "head_map_interleaved":
+        monkeypatch.setattr(A, "_kv_head", lambda hq, Hq, Hkv: hq % Hkv)
+    elif which == "scale_squared":
+        monkeypatch.setattr(A, "_as_f64_scale", lambda s: float(np.float32(s)) ** 2)
+
+
+@pytest.mark.parametrize("which", ["head_map_interleaved", "scale_squared"])
+def test_row_pin_catches_planted_mistakes(monkeypatch, which):
+    w = make_custom([23, 40], 2, 16, 56, pool_pages=6)
+    kp, vp = w.pools()
+    refs = {(b, h): np.array(brute_force(w, b, h)) for b in range(2) for h in range(16)}
+    _plant_row_state(monkeypatch, which)
+    caught = False
+    for (b, h), ref in refs.items():
+        row = oracle.decode_attention_row(w.q, kp, vp, w.block_table, w.context_lens, w.scale, b, h)
+        caught |= not np.allclose(row, ref, rtol=1e-6)
+    assert caught
+
+
+def test_state_pin_catches_planted_scale(monkeypatch):
+    w = make_custom([40], 2, 16, 57, pool_pages=4)
+    kp, vp = w.pools()
+    K = A.gather_tokens(kp, w.block_table, 0, 1, 40)
+    V = A.gather_tokens(vp, w.block_table, 0, 1, 40)
+    bm, bl, bo = brute_force_state(w, 0, 11)
+    _plant_row_state(monkeypatch, "scale_squared")
+    m, l, o = oracle.partial_state(w.q[0, 11], K, V, w.scale)
+    assert abs(m - bm) > 1e-6 * max(abs(bm), 1.0)
+    assert not np.allclose(oracle.merge_states([(m, l, o)]), np.array(brute_force(w, 0, 11)), rtol=1e-6)
