@@ -5,6 +5,7 @@
 // never a silent no-launch, no environment reads in native code).
 
 #include <algorithm>
+#include <limits.h>
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
@@ -15,17 +16,25 @@
 #include "xqa_internal.h"
 #include "xqa_select.h"
 
+// Sizes derived from a configuration and the device: the split grid, the
+// split-state records and the combine kernel's shape.
+struct Geometry {
+  int grid;             // split workgroups = work-item capacity
+  int per_head;         // grid / Hkv
+  int item_stride;      // floats per split-state record
+  int max_q;            // query tokens per sequence the records are sized for
+  int combine_waves;    // waves per combine workgroup
+  bool direct_only;     // no sequence can leave split states: one kernel per step
+  size_t partial_bytes; // 2 * grid records
+};
+
 struct xqa_handle_s {
   xqa_config_t cfg;
   int device;
-  int grid;          // split workgroups = work-item capacity
-  int per_head;      // grid / Hkv
-  int item_stride;   // floats per partial record
-  int combine_waves; // waves per combine workgroup
-  bool direct_only;  // no sequence can leave split states: one kernel per step
-  float* partials;   // workspace: grid partial records
-  int32_t* vtable;   // page-subset decode: [max_batch][max_selected_pages] page ids, then
-  int32_t* vlens;    //   [max_batch] lengths (null when max_selected_pages is 0)
+  Geometry geo;
+  float* partials;    // workspace: 2 * grid split-state records
+  int32_t* vtable;    // page-subset decode: [max_batch][max_selected_pages] page ids, then
+  int32_t* vlens;     //   [max_batch] lengths (null when max_selected_pages is 0)
   size_t workspace_bytes;
 };
 
@@ -75,7 +84,8 @@ xqa_status_t check_device(xqa_handle_t h) {
   return XQA_OK;
 }
 
-xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_pages,
+xqa::AttendArgs attend_args(const xqa_config_t& cfg, const Geometry& geo, float* partials,
+                            const void* q, const uint8_t* k_pages,
                             const uint8_t* v_pages, const int32_t* block_table,
                             const int32_t* context_lens, int32_t batch, float scale, void* out,
                             int32_t q_tokens = 1) {
@@ -86,24 +96,122 @@ xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_page
   a.block_table = block_table;
   a.context_lens = context_lens;
   a.out = static_cast<uint16_t*>(out);
-  a.partials = h->partials;
+  a.partials = partials;
   a.batch = batch;
-  a.num_kv_heads = h->cfg.num_kv_heads;
-  a.group = h->cfg.num_q_heads / h->cfg.num_kv_heads;
+  a.num_kv_heads = cfg.num_kv_heads;
+  a.group = cfg.num_q_heads / cfg.num_kv_heads;
   a.q_tokens = q_tokens;
   a.rows = a.group * q_tokens;
-  a.max_pages = h->cfg.max_pages_per_seq;
-  a.max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
-  a.per_head = h->per_head;
-  a.item_stride = h->item_stride;
-  a.combine_waves = h->combine_waves;
-  a.zero_empty = h->direct_only ? 1 : 0;
+  a.max_pages = cfg.max_pages_per_seq;
+  a.max_tokens = cfg.max_pages_per_seq * xqa::kPageSize;
+  a.per_head = geo.per_head;
+  a.item_stride = geo.item_stride;
+  a.combine_waves = geo.combine_waves;
+  a.zero_empty = geo.direct_only ? 1 : 0;
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.v_scale = 1.0f;
   a.kv_format = xqa::kKvE5M2;
   a.k_new = nullptr;
   a.v_new = nullptr;
   return a;
+}
+
+xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_pages,
+                            const uint8_t* v_pages, const int32_t* block_table,
+                            const int32_t* context_lens, int32_t batch, float scale, void* out,
+                            int32_t q_tokens = 1) {
+  return attend_args(h->cfg, h->geo, h->partials, q, k_pages, v_pages, block_table, context_lens,
+                     batch, scale, out, q_tokens);
+}
+
+// Validation of a configuration.
+xqa_status_t check_config(const xqa_config_t* cfg) {
+  if (cfg->max_batch < 1 || cfg->num_q_heads < 1 || cfg->num_kv_heads < 1 ||
+      cfg->max_pages_per_seq < 1 || cfg->max_work_items < 0 || cfg->max_query_tokens < 0 ||
+      cfg->max_selected_pages < 0)
+    return fail(XQA_ERR_INVALID_ARG, "sizes must be positive");
+  if (cfg->max_selected_pages > cfg->max_pages_per_seq)
+    return fail(XQA_ERR_UNSUPPORTED, "max_selected_pages above max_pages_per_seq");
+  if (cfg->head_dim != xqa::kHeadDim) return fail(XQA_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (cfg->page_size != xqa::kPageSize) return fail(XQA_ERR_UNSUPPORTED, "page_size must be 16");
+  if (cfg->num_q_heads % cfg->num_kv_heads != 0)
+    return fail(XQA_ERR_UNSUPPORTED, "num_q_heads must be a multiple of num_kv_heads");
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  if (G > xqa::kMaxGroup) return fail(XQA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+  const int max_q = cfg->max_query_tokens == 0 ? 1 : cfg->max_query_tokens;
+  if ((long long)G * max_q > xqa::kMaxGroup)
+    return fail(XQA_ERR_UNSUPPORTED,
+                "query heads per KV head times max_query_tokens must not exceed 16");
+  if (cfg->max_batch > xqa::kMaxBatch) return fail(XQA_ERR_UNSUPPORTED, "max_batch above 65536");
+  if ((long long)cfg->max_pages_per_seq * xqa::kPageSize > xqa::kMaxSeqTokens)
+    return fail(XQA_ERR_UNSUPPORTED, "max_pages_per_seq * page_size must not exceed 2^24 tokens");
+  // Every launch's grid must fit HIP's 2^31 - 1 workgroups: the combine
+  // kernel runs up to max_batch * Hkv * 8 workgroups, the split kernel at
+  // most Hkv * 2048.
+  if ((long long)cfg->max_batch * cfg->num_kv_heads * (xqa::kHeadDim / 16) > INT32_MAX ||
+      (long long)cfg->num_kv_heads * xqa::kMaxItemsPerHead > INT32_MAX)
+    return fail(XQA_ERR_UNSUPPORTED, "max_batch * num_kv_heads too large for one launch grid");
+  const long long min_grid = cfg->num_kv_heads;
+  const long long max_grid = (long long)cfg->num_kv_heads * xqa::kMaxItemsPerHead;
+  if (cfg->max_work_items > 0 &&
+      (cfg->max_work_items < min_grid || cfg->max_work_items > max_grid))
+    return fail(XQA_ERR_INVALID_ARG, "max_work_items must lie in [Hkv, Hkv*2048]");
+  return XQA_OK;
+}
+
+// Sizes of a validated configuration on a device with `cus` compute units
+// and `per_cu` resident split workgroups per CU.
+Geometry geometry(const xqa_config_t& cfg, int cus, int per_cu) {
+  Geometry g;
+  const long long min_grid = cfg.num_kv_heads;
+  const long long max_grid = (long long)cfg.num_kv_heads * xqa::kMaxItemsPerHead;
+  const int32_t max_tokens = (int32_t)((long long)cfg.max_pages_per_seq * xqa::kPageSize);
+  long long grid = cfg.max_work_items;
+  if (grid == 0) {
+    // Every item resident at once: one round of equal-sized items, the same
+    // number on every CU.
+    grid = (long long)cus * (per_cu < 1 ? 1 : per_cu);
+    // A step never has more than max_batch full sequences, so it never plans
+    // more than ceil(NB_max / 8) items per head; slots past that would only
+    // be dispatched to exit (a few microseconds on small workloads).
+    const long long nb_max = (long long)cfg.max_batch * xqa::seq_blocks(max_tokens);
+    const long long useful = (long long)cfg.num_kv_heads *
+                             ((nb_max + xqa::kMinItemBlocks - 1) / xqa::kMinItemBlocks);
+    if (grid > useful) grid = useful;
+    if (grid < min_grid) grid = min_grid;
+    if (grid > max_grid) grid = max_grid;
+  }
+  g.per_head = (int)(grid / cfg.num_kv_heads);
+  g.grid = g.per_head * cfg.num_kv_heads;
+  const int G = cfg.num_q_heads / cfg.num_kv_heads;
+  g.max_q = cfg.max_query_tokens == 0 ? 1 : cfg.max_query_tokens;
+  // A record holds O, max and sum of every query row: G * max_query_tokens rows.
+  g.item_stride = ((G * g.max_q * (xqa::kHeadDim + 2)) + 3) / 4 * 4;
+  // Two record slots per work item: its first and its last segment.
+  g.partial_bytes = (size_t)2 * g.grid * g.item_stride * sizeof(float);
+  // A sequence leaves at most one split state per item and per block, so a
+  // handle whose bound stays within one combine round gets the one-wave
+  // combine workgroups; a longer one shares the rounds over four waves.
+  const int max_states = std::min(g.per_head, xqa::seq_blocks(max_tokens));
+  g.combine_waves = max_states > xqa::kCombineRound ? xqa::kCombineMaxWaves : 1;
+  // With one state per sequence at most, every sequence is finished in the
+  // split kernel, which then also writes the zero rows of empty sequences:
+  // a decode step is one kernel.
+  g.direct_only = max_states <= 1;
+  return g;
+}
+
+xqa_status_t device_geometry(const xqa_config_t& cfg, int* dev, Geometry* geo) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, *dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  int per_cu = 0;
+  e = xqa::attend_blocks_per_cu(&per_cu);
+  if (e != hipSuccess) return hip_fail(e, "occupancy query");
+  *geo = geometry(cfg, cus, per_cu);
+  return XQA_OK;
 }
 
 }  // namespace
@@ -125,93 +233,28 @@ const char* xqa_last_error(void) { return g_last_error; }
 
 xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
   if (!cfg || !out_handle) return fail(XQA_ERR_INVALID_ARG, "null cfg or out_handle");
-  if (cfg->max_batch < 1 || cfg->num_q_heads < 1 || cfg->num_kv_heads < 1 ||
-      cfg->max_pages_per_seq < 1 || cfg->max_work_items < 0 || cfg->max_query_tokens < 0 ||
-      cfg->max_selected_pages < 0)
-    return fail(XQA_ERR_INVALID_ARG, "sizes must be positive");
-  if (cfg->max_selected_pages > cfg->max_pages_per_seq)
-    return fail(XQA_ERR_UNSUPPORTED, "max_selected_pages above max_pages_per_seq");
-  if (cfg->head_dim != xqa::kHeadDim) return fail(XQA_ERR_UNSUPPORTED, "head_dim must be 128");
-  if (cfg->page_size != xqa::kPageSize) return fail(XQA_ERR_UNSUPPORTED, "page_size must be 16");
-  if (cfg->num_q_heads % cfg->num_kv_heads != 0)
-    return fail(XQA_ERR_UNSUPPORTED, "num_q_heads must be a multiple of num_kv_heads");
-  const int G = cfg->num_q_heads / cfg->num_kv_heads;
-  if (G > xqa::kMaxGroup) return fail(XQA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
-  const int max_q = cfg->max_query_tokens == 0 ? 1 : cfg->max_query_tokens;
-  if ((long long)G * max_q > xqa::kMaxGroup)
-    return fail(XQA_ERR_UNSUPPORTED,
-                "query heads per KV head times max_query_tokens must not exceed 16");
-  if (cfg->max_batch > xqa::kMaxBatch) return fail(XQA_ERR_UNSUPPORTED, "max_batch above 65536");
-  if ((long long)cfg->max_pages_per_seq * xqa::kPageSize > xqa::kMaxSeqTokens)
-    return fail(XQA_ERR_UNSUPPORTED, "max_pages_per_seq * page_size must not exceed 2^24 tokens");
-  const long long min_grid = cfg->num_kv_heads;
-  const long long max_grid = (long long)cfg->num_kv_heads * xqa::kMaxItemsPerHead;
-  if (cfg->max_work_items > 0 &&
-      (cfg->max_work_items < min_grid || cfg->max_work_items > max_grid))
-    return fail(XQA_ERR_INVALID_ARG, "max_work_items must lie in [Hkv, Hkv*2048]");
-
+  xqa_status_t st = check_config(cfg);
+  if (st != XQA_OK) return st;
   int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  int cus = 0;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-  int per_cu = 0;
-  e = xqa::attend_blocks_per_cu(&per_cu);
-  if (e != hipSuccess) return hip_fail(e, "occupancy query");
-  if (per_cu < 1) per_cu = 1;
-
-  long long grid = cfg->max_work_items;
-  if (grid == 0) {
-    // Every item resident at once: one round of equal-sized items, the same
-    // number on every CU.
-    grid = (long long)cus * per_cu;
-    // A step never has more than max_batch full sequences, so it never plans
-    // more than ceil(NB_max / 8) items per head; slots past that would only
-    // be dispatched to exit (a few microseconds on small workloads).
-    const long long nb_max =
-        (long long)cfg->max_batch *
-        xqa::seq_blocks((int32_t)((long long)cfg->max_pages_per_seq * xqa::kPageSize));
-    const long long useful = (long long)cfg->num_kv_heads *
-                             ((nb_max + xqa::kMinItemBlocks - 1) / xqa::kMinItemBlocks);
-    if (grid > useful) grid = useful;
-    if (grid < min_grid) grid = min_grid;
-    if (grid > max_grid) grid = max_grid;
-  }
-  const int per_head = (int)(grid / cfg->num_kv_heads);
-  grid = (long long)per_head * cfg->num_kv_heads;
-  // A record holds O, max and sum of every query row: G * max_query_tokens rows.
-  const int stride = ((G * max_q * (xqa::kHeadDim + 2)) + 3) / 4 * 4;
-  // Two record slots per work item: its first and its last segment.
-  const size_t ws = (size_t)2 * grid * stride * sizeof(float);
+  Geometry geo;
+  if ((st = device_geometry(*cfg, &dev, &geo)) != XQA_OK) return st;
 
   xqa_handle_s* h = new (std::nothrow) xqa_handle_s();
   if (!h) return fail(XQA_ERR_OUT_OF_MEMORY, "host allocation failed");
   h->cfg = *cfg;
-  h->cfg.max_query_tokens = max_q;
+  h->cfg.max_query_tokens = geo.max_q;
   h->device = dev;
-  h->grid = (int)grid;
-  h->per_head = per_head;
-  h->item_stride = stride;
-  // A sequence leaves at most one split state per item and per block, so a
-  // handle whose bound stays within one combine round gets the one-wave
-  // combine workgroups; a longer one shares the rounds over four waves.
-  const int max_states = std::min(per_head, xqa::seq_blocks(
-      (int32_t)((long long)cfg->max_pages_per_seq * xqa::kPageSize)));
-  h->combine_waves = max_states > xqa::kCombineRound ? xqa::kCombineMaxWaves : 1;
-  // With one state per sequence at most, every sequence is finished in the
-  // split kernel, which then also writes the zero rows of empty sequences:
-  // a decode step is one kernel.
-  h->direct_only = max_states <= 1;
+  h->geo = geo;
   // Page-subset decode: a page table of max_batch rows plus their lengths.
   const size_t vt_elems = cfg->max_selected_pages > 0
                               ? (size_t)cfg->max_batch * cfg->max_selected_pages + cfg->max_batch
                               : 0;
+  const size_t ws = geo.partial_bytes;
   h->workspace_bytes = ws + vt_elems * sizeof(int32_t);
   h->partials = nullptr;
   h->vtable = nullptr;
   h->vlens = nullptr;
-  e = hipMalloc(reinterpret_cast<void**>(&h->partials), ws);
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->partials), ws);
   if (e == hipSuccess && vt_elems > 0) {
     e = hipMalloc(reinterpret_cast<void**>(&h->vtable), vt_elems * sizeof(int32_t));
     if (e == hipSuccess) h->vlens = h->vtable + (size_t)cfg->max_batch * cfg->max_selected_pages;
@@ -220,7 +263,7 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
     if (h->partials) (void)hipFree(h->partials);
     delete h;
     if (e == hipErrorOutOfMemory) return fail(XQA_ERR_OUT_OF_MEMORY, "workspace allocation failed");
-    return hip_fail(e, "hipMalloc");
+    return hip_fail(e, "workspace allocation");
   }
 
   *out_handle = h;
@@ -243,13 +286,13 @@ xqa_status_t xqa_destroy(xqa_handle_t h) {
 xqa_status_t xqa_get_info(xqa_handle_t h, xqa_info_t* info) {
   if (!h || !info) return fail(XQA_ERR_INVALID_ARG, "null handle or info");
   info->device = h->device;
-  info->max_work_items = h->grid;
-  info->items_per_head = h->per_head;
+  info->max_work_items = h->geo.grid;
+  info->items_per_head = h->geo.per_head;
   info->token_granule = xqa::kBlockTokens;
   info->threads_per_item = xqa::kThreads;
-  info->item_stride_floats = h->item_stride;
+  info->item_stride_floats = h->geo.item_stride;
   info->workspace_bytes = (int64_t)h->workspace_bytes;
-  info->kernels_per_step = h->direct_only ? 1 : 2;
+  info->kernels_per_step = h->geo.direct_only ? 1 : 2;
   return XQA_OK;
 }
 
@@ -263,7 +306,7 @@ xqa_status_t xqa_decode_split(xqa_handle_t h, const void* q, const uint8_t* k_pa
   if ((st = check_device(h)) != XQA_OK) return st;
   const xqa::AttendArgs a =
       attend_args(h, q, k_pages, v_pages, block_table, context_lens, batch, scale, out);
-  hipError_t e = xqa::launch_split(a, h->grid, static_cast<hipStream_t>(stream));
+  hipError_t e = xqa::launch_split(a, h->geo.grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
   return XQA_OK;
 }
@@ -323,9 +366,9 @@ xqa_status_t xqa_decode_fp8(xqa_handle_t h, xqa_kv_format_t kv_format, const voi
   a.v_scale = v_scale;
   a.kv_format = kv_format == XQA_KV_E4M3 ? xqa::kKvE4M3 : xqa::kKvE5M2;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = xqa::launch_split(a, h->grid, s);
+  hipError_t e = xqa::launch_split(a, h->geo.grid, s);
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
-  if (h->direct_only) return XQA_OK;
+  if (h->geo.direct_only) return XQA_OK;
   e = xqa::launch_combine(a, s);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return XQA_OK;
@@ -377,9 +420,9 @@ xqa_status_t xqa_decode_append(xqa_handle_t h, const void* q, const void* k_new,
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = xqa::launch_split(a, h->grid, s);
+  hipError_t e = xqa::launch_split(a, h->geo.grid, s);
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
-  if (h->direct_only) return XQA_OK;
+  if (h->geo.direct_only) return XQA_OK;
   e = xqa::launch_combine(a, s);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return XQA_OK;
@@ -421,9 +464,9 @@ xqa_status_t xqa_decode_pages(xqa_handle_t h, const void* q, const uint8_t* k_pa
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = xqa::launch_select(sa, s);
   if (e != hipSuccess) return hip_fail(e, "select kernel launch");
-  e = xqa::launch_split(a, h->grid, s);
+  e = xqa::launch_split(a, h->geo.grid, s);
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
-  if (h->direct_only) return XQA_OK;
+  if (h->geo.direct_only) return XQA_OK;
   e = xqa::launch_combine(a, s);
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   return XQA_OK;
@@ -438,7 +481,7 @@ xqa_status_t xqa_plan(xqa_handle_t h, const int32_t* ctx, int32_t batch, int32_t
   const int max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
   long long nb_total = 0;
   for (int b = 0; b < batch; ++b) nb_total += xqa::seq_blocks(xqa::clamp_len(ctx[b], max_tokens));
-  const int P = xqa::items_per_head(nb_total, h->per_head);
+  const int P = xqa::items_per_head(nb_total, h->geo.per_head);
   *split_tokens = P > 0 ? (int32_t)((nb_total + P - 1) / P * xqa::kBlockTokens) : 0;
   *num_items = P * h->cfg.num_kv_heads;
   return XQA_OK;

@@ -128,6 +128,9 @@ int main() {
     EXPECT(xqa_create(&c, &h) == XQA_ERR_UNSUPPORTED && h == nullptr);
     c = config(1, 8, 1, (1 << 20) + 1);
     EXPECT(xqa_create(&c, &h) == XQA_ERR_UNSUPPORTED && h == nullptr);
+    // The combine grid (max_batch * Hkv * 8 workgroups) must fit one launch.
+    c = config(65536, 4097, 4097, 1);
+    EXPECT(xqa_create(&c, &h) == XQA_ERR_UNSUPPORTED && h == nullptr);
     EXPECT(xqa_create(nullptr, &h) == XQA_ERR_INVALID_ARG);
     EXPECT(std::strlen(xqa_last_error()) > 0);
   }
