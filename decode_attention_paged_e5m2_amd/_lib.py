@@ -13,7 +13,7 @@ XQA_ERR_OUT_OF_MEMORY = 3
 XQA_ERR_HIP = 4
 
 EXPORTED = [
-    "xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_multi",
+    "xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_noalloc", "xqa_decode_multi",
     "xqa_decode_fp8", "xqa_decode_append", "xqa_decode_pages", "xqa_decode_split",
     "xqa_decode_combine", "xqa_append_kv", "xqa_plan", "xqa_debug_widen_e5m2",
     "xqa_debug_widen_e4m3", "xqa_status_string", "xqa_last_error",
@@ -72,6 +72,7 @@ def load() -> ctypes.CDLL:
     lib.xqa_get_info.argtypes = [vp, ctypes.POINTER(XqaInfo)]
     dec = [vp, vp, vp, vp, vp, vp, i32, f32, vp, vp]
     lib.xqa_decode.argtypes = dec
+    lib.xqa_decode_noalloc.argtypes = [ctypes.POINTER(XqaConfig)] + dec[1:]
     lib.xqa_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp]
     lib.xqa_decode_fp8.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, f32, f32, f32,
                                    vp, vp]
@@ -87,7 +88,8 @@ def load() -> ctypes.CDLL:
     lib.xqa_status_string.restype = ctypes.c_char_p
     lib.xqa_last_error.argtypes = []
     lib.xqa_last_error.restype = ctypes.c_char_p
-    for name in ("xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_multi",
+    for name in ("xqa_create", "xqa_destroy", "xqa_get_info", "xqa_decode", "xqa_decode_noalloc",
+                 "xqa_decode_multi",
                  "xqa_decode_fp8", "xqa_debug_widen_e4m3", "xqa_decode_append", "xqa_decode_pages",
                  "xqa_decode_split",
                  "xqa_decode_combine", "xqa_append_kv", "xqa_plan", "xqa_debug_widen_e5m2"):

@@ -12,7 +12,7 @@ INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_NAME = "libxqa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "xqa_kernels.hip"), os.path.join(CSRC, "xqa_select.hip"),
-           os.path.join(CSRC, "xqa_api.cpp")]
+           os.path.join(CSRC, "xqa_noalloc.hip"), os.path.join(CSRC, "xqa_api.cpp")]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for all device code. MFMA results

@@ -14,6 +14,7 @@
 
 #include "../../include/xqa.h"
 #include "xqa_internal.h"
+#include "xqa_noalloc.h"
 #include "xqa_select.h"
 
 // Sizes derived from a configuration and the device: the split grid, the
@@ -124,7 +125,7 @@ xqa::AttendArgs attend_args(xqa_handle_t h, const void* q, const uint8_t* k_page
                      batch, scale, out, q_tokens);
 }
 
-// Validation of a configuration.
+// Validation shared by xqa_create and xqa_decode_noalloc.
 xqa_status_t check_config(const xqa_config_t* cfg) {
   if (cfg->max_batch < 1 || cfg->num_q_heads < 1 || cfg->num_kv_heads < 1 ||
       cfg->max_pages_per_seq < 1 || cfg->max_work_items < 0 || cfg->max_query_tokens < 0 ||
@@ -334,6 +335,44 @@ xqa_status_t xqa_decode(xqa_handle_t h, const void* q, const uint8_t* k_pages,
                         void* stream) {
   return xqa_decode_multi(h, q, k_pages, v_pages, block_table, context_lens, batch, 1, scale, out,
                           stream);
+}
+
+xqa_status_t xqa_decode_noalloc(const xqa_config_t* cfg, const void* q, const uint8_t* k_pages,
+                                const uint8_t* v_pages, const int32_t* block_table,
+                                const int32_t* context_lens, int32_t batch, float scale, void* out,
+                                void* stream) {
+  if (!cfg) return fail(XQA_ERR_INVALID_ARG, "null cfg");
+  xqa_status_t st = check_config(cfg);
+  if (st != XQA_OK) return st;
+  if (!q || !k_pages || !v_pages || !block_table || !context_lens || !out)
+    return fail(XQA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16))
+    return fail(XQA_ERR_INVALID_ARG, "q, k_pages, v_pages and out must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4))
+    return fail(XQA_ERR_INVALID_ARG, "block_table and context_lens must be 4-byte aligned");
+  if (batch < 1 || batch > cfg->max_batch)
+    return fail(XQA_ERR_INVALID_ARG, "batch outside [1, max_batch]");
+  if (!isfinite(scale)) return fail(XQA_ERR_INVALID_ARG, "scale must be finite");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  xqa::NoallocDevice nd;
+  e = xqa::noalloc_device(dev, &nd);
+  if (e != hipSuccess) return hip_fail(e, "fixed workspace lookup");
+  const Geometry geo = geometry(*cfg, nd.cus, nd.per_cu);
+  if (geo.partial_bytes > xqa::kNoallocScratchBytes)
+    return fail(XQA_ERR_UNSUPPORTED,
+                "the configuration's split states exceed the fixed 16 MiB workspace "
+                "(fewer max_work_items, KV heads or query rows)");
+  const xqa::AttendArgs a = attend_args(*cfg, geo, static_cast<float*>(nd.scratch), q, k_pages,
+                                        v_pages, block_table, context_lens, batch, scale, out);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  e = xqa::launch_split(a, geo.grid, s);
+  if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+  if (geo.direct_only) return XQA_OK;
+  e = xqa::launch_combine(a, s);
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return XQA_OK;
 }
 
 xqa_status_t xqa_decode_multi(xqa_handle_t h, const void* q, const uint8_t* k_pages,

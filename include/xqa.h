@@ -130,6 +130,29 @@ xqa_status_t xqa_decode(xqa_handle_t handle, const void* q, const uint8_t* k_pag
                         const int32_t* context_lens, int32_t batch, float scale,
                         void* out, void* stream);
 
+/* xqa_decode without a handle, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. The split-state records live in a fixed 16 MiB device
+ * array inside the library (one per GPU, held until the process ends)
+ * instead of a handle's workspace; nothing is allocated, here or later. cfg
+ * (host memory) is validated as by xqa_create and sizes the step exactly as
+ * a handle made from it would, so the output is bitwise that of xqa_decode
+ * on such a handle. The first call on a device looks up the array's address
+ * on that device (the calling thread's current device) and keeps it. Every
+ * call on one GPU shares that GPU's array: calls on one stream are ordered
+ * and safe; calls that overlap in time on one GPU (other streams, other
+ * threads) race and give undefined results. Nothing in the array needs to
+ * start at zero: every record a call reads, the same call wrote. Limit:
+ * 2 * split grid * record floats * 4 bytes must fit 16 MiB (the default
+ * grid on one MI355X does for every supported head shape). Arguments,
+ * alignment and errors as for xqa_decode, with cfg's max_batch;
+ * INVALID_ARG / UNSUPPORTED as for xqa_create; UNSUPPORTED also when the
+ * records do not fit the fixed array. */
+xqa_status_t xqa_decode_noalloc(const xqa_config_t* cfg, const void* q, const uint8_t* k_pages,
+                                const uint8_t* v_pages, const int32_t* block_table,
+                                const int32_t* context_lens, int32_t batch, float scale,
+                                void* out, void* stream);
+
 /* Several new query tokens per sequence (speculative or multi-token
  * prediction rows, which the page "[Kernel][SM70] Pipeline batched E5M2 XQA
  * decode" lists beside single-token decode in its Purpose), causal among

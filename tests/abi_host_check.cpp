@@ -12,6 +12,7 @@
 
 #include "xqa.h"
 #include "xqa_internal.h"
+#include "xqa_noalloc.h"
 #include "xqa_select.h"
 
 namespace {
@@ -85,6 +86,16 @@ hipError_t launch_widen(const uint8_t*, uint16_t*, float*, int64_t, int32_t, hip
 hipError_t attend_blocks_per_cu(int* blocks) {
   *blocks = 2;
   return hipSuccess;
+}
+// The fixed workspace: a stand-in address; xqa_decode_noalloc only passes it on.
+alignas(256) unsigned char g_fixed[64];
+int g_noalloc_lookups = 0;
+hipError_t noalloc_device(int device, NoallocDevice* out) {
+  ++g_noalloc_lookups;
+  out->scratch = g_fixed;
+  out->cus = 256;
+  out->per_cu = 2;
+  return device == 0 ? hipSuccess : hipErrorInvalidDevice;
 }
 }  // namespace xqa
 
@@ -241,6 +252,48 @@ int main() {
          XQA_ERR_UNSUPPORTED);
   EXPECT(xqa_destroy(h) == XQA_OK);
   EXPECT(xqa_destroy(nullptr) == XQA_OK);
+
+  // The handle-free decode: same grid and launches as a handle from the same
+  // configuration, split states in the fixed workspace; rejected calls and
+  // steps past the fixed workspace launch nothing.
+  {
+    xqa_config_t cn = config(16, 32, 4, 16384);
+    g_launches.clear();
+    EXPECT(xqa_decode_noalloc(&cn, p16, kv, kv, i32, i32, 16, 0.1f, p16, nullptr) == XQA_OK);
+    EXPECT(g_launches.size() == 2 && g_launches[0].kind == 's' && g_launches[1].kind == 'c');
+    if (g_launches.size() == 2) {
+      EXPECT(g_launches[0].grid == 512 && g_launches[0].a.per_head == 128);
+      EXPECT((void*)g_launches[0].a.partials == (void*)xqa::g_fixed);
+      EXPECT(g_launches[1].a.partials == g_launches[0].a.partials);
+      EXPECT(g_launches[0].a.batch == 16 && g_launches[0].a.group == 8);
+    }
+    g_launches.clear();
+    EXPECT(xqa_decode_noalloc(nullptr, p16, kv, kv, i32, i32, 16, 0.1f, p16, nullptr) ==
+           XQA_ERR_INVALID_ARG);
+    EXPECT(xqa_decode_noalloc(&cn, p16, kv, kv, i32, i32, 17, 0.1f, p16, nullptr) ==
+           XQA_ERR_INVALID_ARG);
+    EXPECT(xqa_decode_noalloc(&cn, odd, kv, kv, i32, i32, 4, 0.1f, p16, nullptr) ==
+           XQA_ERR_INVALID_ARG);
+    EXPECT(xqa_decode_noalloc(&cn, p16, kv, kv, i32, i32, 4, NAN, p16, nullptr) ==
+           XQA_ERR_INVALID_ARG);
+    xqa_config_t bad = cn;
+    bad.head_dim = 64;
+    EXPECT(xqa_decode_noalloc(&bad, p16, kv, kv, i32, i32, 4, 0.1f, p16, nullptr) ==
+           XQA_ERR_UNSUPPORTED);
+    // 2048 items per KV head of 16 query rows: 2 * 8192 records of 2080
+    // floats, past 16 MiB.
+    bad = config(4, 64, 4, 64);
+    bad.max_work_items = 4 * 2048;
+    EXPECT(xqa_decode_noalloc(&bad, p16, kv, kv, i32, i32, 4, 0.1f, p16, nullptr) ==
+           XQA_ERR_UNSUPPORTED);
+    EXPECT(std::strstr(xqa_last_error(), "16 MiB") != nullptr);
+    EXPECT(g_launches.empty());
+    // A handle-free call on a one-kernel configuration launches one kernel.
+    xqa_config_t one = config(100, 16, 2, 2);
+    EXPECT(xqa_decode_noalloc(&one, p16, kv, kv, i32, i32, 100, 0.1f, p16, nullptr) == XQA_OK);
+    EXPECT(g_launches.size() == 1 && g_launches[0].a.zero_empty == 1);
+    EXPECT(xqa::g_noalloc_lookups > 0);
+  }
 
   if (g_fail) return 1;
   std::printf("OK %d checks\n", g_checks);
