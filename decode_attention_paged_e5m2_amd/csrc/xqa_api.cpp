@@ -27,13 +27,14 @@ struct Geometry {
   int combine_waves;    // waves per combine workgroup
   bool direct_only;     // no sequence can leave split states: one kernel per step
   size_t partial_bytes; // 2 * grid records
+  size_t prefix_bytes;  // batches over 64: per-chunk block prefix table, after the records
 };
 
 struct xqa_handle_s {
   xqa_config_t cfg;
   int device;
   Geometry geo;
-  float* partials;    // workspace: 2 * grid split-state records
+  float* partials;    // workspace: 2 * grid split-state records, then the chunk prefix table
   int32_t* vtable;    // page-subset decode: [max_batch][max_selected_pages] page ids, then
   int32_t* vlens;     //   [max_batch] lengths (null when max_selected_pages is 0)
   size_t workspace_bytes;
@@ -85,7 +86,7 @@ xqa_status_t check_device(xqa_handle_t h) {
   return XQA_OK;
 }
 
-xqa::AttendArgs attend_args(const xqa_config_t& cfg, const Geometry& geo, float* partials,
+xqa::AttendArgs attend_args(const xqa_config_t& cfg, const Geometry& geo, void* workspace,
                             const void* q, const uint8_t* k_pages,
                             const uint8_t* v_pages, const int32_t* block_table,
                             const int32_t* context_lens, int32_t batch, float scale, void* out,
@@ -97,7 +98,10 @@ xqa::AttendArgs attend_args(const xqa_config_t& cfg, const Geometry& geo, float*
   a.block_table = block_table;
   a.context_lens = context_lens;
   a.out = static_cast<uint16_t*>(out);
-  a.partials = partials;
+  a.partials = static_cast<float*>(workspace);
+  a.seq_prefix = geo.prefix_bytes > 0
+                     ? reinterpret_cast<long long*>(static_cast<char*>(workspace) + geo.partial_bytes)
+                     : nullptr;
   a.batch = batch;
   a.num_kv_heads = cfg.num_kv_heads;
   a.group = cfg.num_q_heads / cfg.num_kv_heads;
@@ -190,6 +194,7 @@ Geometry geometry(const xqa_config_t& cfg, int cus, int per_cu) {
   g.item_stride = ((G * g.max_q * (xqa::kHeadDim + 2)) + 3) / 4 * 4;
   // Two record slots per work item: its first and its last segment.
   g.partial_bytes = (size_t)2 * g.grid * g.item_stride * sizeof(float);
+  g.prefix_bytes = cfg.max_batch > 64 ? ((size_t)(cfg.max_batch + 63) / 64 + 1) * sizeof(long long) : 0;
   // A sequence leaves at most one split state per item and per block, so a
   // handle whose bound stays within one combine round gets the one-wave
   // combine workgroups; a longer one shares the rounds over four waves.
@@ -250,7 +255,7 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
   const size_t vt_elems = cfg->max_selected_pages > 0
                               ? (size_t)cfg->max_batch * cfg->max_selected_pages + cfg->max_batch
                               : 0;
-  const size_t ws = geo.partial_bytes;
+  const size_t ws = geo.partial_bytes + geo.prefix_bytes;
   h->workspace_bytes = ws + vt_elems * sizeof(int32_t);
   h->partials = nullptr;
   h->vtable = nullptr;
@@ -360,11 +365,11 @@ xqa_status_t xqa_decode_noalloc(const xqa_config_t* cfg, const void* q, const ui
   e = xqa::noalloc_device(dev, &nd);
   if (e != hipSuccess) return hip_fail(e, "fixed workspace lookup");
   const Geometry geo = geometry(*cfg, nd.cus, nd.per_cu);
-  if (geo.partial_bytes > xqa::kNoallocScratchBytes)
+  if (geo.partial_bytes + geo.prefix_bytes > xqa::kNoallocScratchBytes)
     return fail(XQA_ERR_UNSUPPORTED,
                 "the configuration's split states exceed the fixed 16 MiB workspace "
                 "(fewer max_work_items, KV heads or query rows)");
-  const xqa::AttendArgs a = attend_args(*cfg, geo, static_cast<float*>(nd.scratch), q, k_pages,
+  const xqa::AttendArgs a = attend_args(*cfg, geo, nd.scratch, q, k_pages,
                                         v_pages, block_table, context_lens, batch, scale, out);
   hipStream_t s = static_cast<hipStream_t>(stream);
   e = xqa::launch_split(a, geo.grid, s);

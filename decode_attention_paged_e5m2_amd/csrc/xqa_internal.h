@@ -74,7 +74,9 @@ struct AttendArgs {
   const int32_t* block_table;
   const int32_t* context_lens;
   uint16_t* out;
-  float* partials;        // [grid][item_stride] split states
+  float* partials;        // [2 * grid][item_stride] split states
+  long long* seq_prefix;  // batches over 64: [ceil(batch / 64) + 1] blocks before each 64-sequence
+                          // chunk, written by the split kernel, read by the combine kernel
   int32_t batch;
   int32_t num_kv_heads;
   int32_t group;

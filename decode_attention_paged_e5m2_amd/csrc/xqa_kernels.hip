@@ -171,17 +171,15 @@ __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
 }
 
 // ---------------------------------------------------------------- the plan
-// Wave-level evaluation of the balanced plan (see xqa_internal.h). Each lane
-// reads the length of one sequence per 64-sequence chunk and every call costs
-// one pass over context_lens.
+// Wave-level evaluation of the balanced plan (see xqa_internal.h).
 //
 // Inclusive prefix sum over the wave with DPP alone (no LDS round trip):
 // shifts by 1, 2, 4 and 8 lanes inside each row of 16 (lanes with no source
 // add 0) give row prefixes; then the last lane of row 0 is added to row 1 and
 // that of row 2 to row 3 (row_bcast:15), and lane 31 to rows 2 and 3
-// (row_bcast:31).
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-  (void)lane;
+// (row_bcast:31). Sums wrap modulo 2^32, so unsigned totals up to 2^32 - 1
+// are exact when read back as unsigned.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
   v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
   v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
@@ -191,104 +189,148 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-__device__ __forceinline__ long long uniform64(long long v) {
-  const int lo = __builtin_amdgcn_readfirstlane((int)(v & 0xFFFFFFFFll));
-  const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
-  return ((long long)hi << 32) | (unsigned)lo;
-}
-
-// Total 32-token blocks per head: NB = sum_b ceil(n_b / 32).
-__device__ long long plan_total_blocks(const int32_t* ctx, int batch, int max_tokens, int lane) {
-  long long sum = 0;
-  for (int base = 0; base < batch; base += 64) {
-    const int i = base + lane;
-    sum += i < batch ? seq_blocks(clamp_len(ctx[i], max_tokens)) : 0;
-  }
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-  return uniform64(sum);
-}
-
 struct SeqInfo {
   int b;          // sequence index
   int n;          // clamped length
   long long off;  // first block in the head's block stream
 };
 
-// Sequence b's length and block offset.
-__device__ SeqInfo seq_at(const int32_t* ctx, int batch, int max_tokens, int b, int lane) {
-  long long prefix = 0;
-  for (int base = 0; base < batch; base += 64) {
-    const int i = base + lane;
-    const int n = i < batch ? clamp_len(ctx[i], max_tokens) : 0;
-    const int nb = seq_blocks(n);
-    const int incl = wave_inclusive_scan(nb, lane);
-    if (b < base + 64) {
-      const int src = b - base;
-      return {b, __builtin_amdgcn_readlane(n, src), prefix + __builtin_amdgcn_readlane(incl - nb, src)};
-    }
-    prefix += __builtin_amdgcn_readlane(incl, 63);
-  }
-  return {b, 0, prefix};
-}
-
-// The non-empty sequence whose blocks contain block x (x < NB).
-__device__ SeqInfo seq_containing(const int32_t* ctx, int batch, int max_tokens, long long x,
-                                  int lane) {
-  long long prefix = 0;
-  for (int base = 0; base < batch; base += 64) {
-    const int i = base + lane;
-    const int n = i < batch ? clamp_len(ctx[i], max_tokens) : 0;
-    const int nb = seq_blocks(n);
-    const int incl = wave_inclusive_scan(nb, lane);
-    const long long lo = prefix + incl - nb;
-    const unsigned long long hit = __ballot(nb > 0 && x >= lo && x < prefix + incl);
-    if (hit) {
-      const int src = __ffsll((unsigned long long)hit) - 1;
-      return {base + src, __builtin_amdgcn_readlane(n, src), prefix + __builtin_amdgcn_readlane(incl - nb, src)};
-    }
-    prefix += __builtin_amdgcn_readlane(incl, 63);
-  }
-  return {batch, 0, prefix};
-}
-
-// The lookups the kernels make, with one pass over context_lens. For
-// batch <= 64 the pass leaves sequence `lane`'s length and block prefix in
-// lane registers, and every later lookup is a v_readlane or a ballot with no
-// memory access; larger batches rescan context_lens per lookup.
+// The lookups the kernels make. For batch <= 64 one pass over context_lens
+// leaves sequence `lane`'s length and block prefix in lane registers, and
+// every later lookup is a v_readlane or a ballot with no memory access.
+// Larger batches keep, per 64-sequence chunk c, the number of blocks before
+// it (off[c], off[nch] = total): the split kernel builds this table once per
+// workgroup in LDS (the four waves share out the chunks, eight chunk loads in
+// flight per wave) and its workgroup 0 copies it to the workspace, where the
+// combine kernel reads it. A lookup is then one load of a chunk's lengths
+// and a scan; finding the chunk that holds a block is a ballot over the
+// table, 64 chunks per step.
 struct SeqTable {
   const int32_t* ctx;
   int batch, max_tokens;
-  bool small;      // batch <= 64
-  int n_l;         // small: clamped length of sequence `lane` (0 past the batch)
-  int excl_l;      // small: first block of sequence `lane`
-  long long nb;    // total blocks per head
+  bool small;               // batch <= 64
+  int n_l;                  // small: clamped length of sequence `lane` (0 past the batch)
+  int excl_l;               // small: first block of sequence `lane`
+  int nch;                  // large: 64-sequence chunks
+  const long long* off;     // large: [nch + 1] blocks before each chunk (LDS or global)
+  long long nb;             // total blocks per head
 
-  __device__ SeqTable(const int32_t* c, int bt, int mt, int lane)
-      : ctx(c), batch(bt), max_tokens(mt), small(bt <= 64), n_l(0), excl_l(0), nb(0) {
+  // Split kernel: called by every thread of the workgroup (the large path
+  // synchronises the workgroup). lds: room for kMaxBatch / 64 + 1 values;
+  // publish: where workgroup 0 copies the table (may be null).
+  __device__ SeqTable(const int32_t* c, int bt, int mt, int lane, int wave, long long* lds)
+      : ctx(c), batch(bt), max_tokens(mt), small(bt <= 64), n_l(0), excl_l(0), nch(0), off(lds),
+        nb(0) {
     if (small) {
-      n_l = lane < batch ? clamp_len(ctx[lane], max_tokens) : 0;
-      const int b_l = seq_blocks(n_l);
-      const int incl = wave_inclusive_scan(b_l, lane);   // <= 64 * 2^19: no overflow
-      excl_l = incl - b_l;
-      nb = __builtin_amdgcn_readlane(incl, 63);
+      init_small(lane);
+      return;
+    }
+    nch = (batch + 63) >> 6;
+    for (int c0 = 8 * wave; c0 < nch; c0 += 8 * kWaves) {
+      int v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {   // unconditional (clamped) loads: all eight in flight
+        const int i = 64 * (c0 + k) + lane;
+        const int n = clamp_len(ctx[min(i, batch - 1)], max_tokens);
+        v[k] = i < batch ? seq_blocks(n) : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const unsigned tot = (unsigned)__builtin_amdgcn_readlane(wave_inclusive_scan(v[k]), 63);
+        if (lane == 0 && c0 + k < nch) lds[c0 + k] = tot;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      long long run = 0;
+      for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int cc = c0 + lane;
+        const unsigned t = cc < nch ? (unsigned)lds[cc] : 0u;
+        const unsigned incl = (unsigned)wave_inclusive_scan((int)t);
+        if (cc < nch) lds[cc] = run + incl - t;
+        run += (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
+      }
+      if (lane == 0) lds[nch] = run;
+    }
+    __syncthreads();
+    nb = lds[nch];
+  }
+
+  // Workgroup 0 of the split kernel copies its table to the workspace for
+  // the combine kernel (batches over 64).
+  __device__ void publish(long long* dst) const {
+    if (small || dst == nullptr || blockIdx.x != 0) return;
+    for (int cc = threadIdx.x; cc <= nch; cc += kThreads) dst[cc] = off[cc];
+  }
+
+  // Combine kernel: the large path reads the table the split kernel published.
+  __device__ SeqTable(const int32_t* c, int bt, int mt, int lane, const long long* published)
+      : ctx(c), batch(bt), max_tokens(mt), small(bt <= 64), n_l(0), excl_l(0), nch(0),
+        off(published), nb(0) {
+    if (small) {
+      init_small(lane);
     } else {
-      nb = plan_total_blocks(ctx, batch, max_tokens, lane);
+      nch = (batch + 63) >> 6;
+      nb = off[nch];
     }
   }
 
-  __device__ SeqInfo at(int b, int lane) const {
-    if (!small) return seq_at(ctx, batch, max_tokens, b, lane);
-    if (b >= 64) return {b, 0, nb};
-    return {b, __builtin_amdgcn_readlane(n_l, b), (long long)__builtin_amdgcn_readlane(excl_l, b)};
+  __device__ void init_small(int lane) {
+    n_l = lane < batch ? clamp_len(ctx[lane], max_tokens) : 0;
+    const int b_l = seq_blocks(n_l);
+    const int incl = wave_inclusive_scan(b_l);   // <= 64 * 2^19: no overflow
+    excl_l = incl - b_l;
+    nb = __builtin_amdgcn_readlane(incl, 63);
   }
 
+  // One 64-sequence chunk: lane's length and its block offset inside the chunk.
+  __device__ void load_chunk(int c, int lane, int& n, int& excl, int& blocks) const {
+    const int i = 64 * c + lane;
+    n = i < batch ? clamp_len(ctx[min(i, batch - 1)], max_tokens) : 0;
+    blocks = seq_blocks(n);
+    excl = (int)((unsigned)wave_inclusive_scan(blocks) - (unsigned)blocks);
+  }
+
+  __device__ SeqInfo at(int b, int lane) const {
+    if (small) {
+      if (b >= 64) return {b, 0, nb};
+      return {b, __builtin_amdgcn_readlane(n_l, b), (long long)__builtin_amdgcn_readlane(excl_l, b)};
+    }
+    if (b >= batch) return {b, 0, nb};
+    const int c = b >> 6;
+    int n, excl, blocks;
+    load_chunk(c, lane, n, excl, blocks);
+    return {b, __builtin_amdgcn_readlane(n, b & 63),
+            off[c] + (unsigned)__builtin_amdgcn_readlane(excl, b & 63)};
+  }
+
+  // The non-empty sequence whose blocks contain block x (x < nb).
   __device__ SeqInfo containing(long long x, int lane) const {
-    if (!small) return seq_containing(ctx, batch, max_tokens, x, lane);
-    const unsigned long long hit =
-        __ballot(n_l > 0 && x >= excl_l && x < excl_l + seq_blocks(n_l));
+    if (small) {
+      const unsigned long long hit =
+          __ballot(n_l > 0 && x >= excl_l && x < excl_l + seq_blocks(n_l));
+      if (!hit) return {batch, 0, nb};
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      return {src, __builtin_amdgcn_readlane(n_l, src), (long long)__builtin_amdgcn_readlane(excl_l, src)};
+    }
+    // The first chunk whose end passes x.
+    int c = nch;
+    for (int g = 0; g < nch; g += 64) {
+      const unsigned long long hit = __ballot(off[min(g + lane + 1, nch)] > x);
+      if (hit) {
+        c = g + __ffsll((unsigned long long)hit) - 1;
+        break;
+      }
+    }
+    if (c >= nch) return {batch, 0, nb};
+    int n, excl, blocks;
+    load_chunk(c, lane, n, excl, blocks);
+    const long long lo = off[c] + (unsigned)excl;
+    const unsigned long long hit = __ballot(blocks > 0 && x >= lo && x < lo + blocks);
     if (!hit) return {batch, 0, nb};
     const int src = __ffsll((unsigned long long)hit) - 1;
-    return {src, __builtin_amdgcn_readlane(n_l, src), (long long)__builtin_amdgcn_readlane(excl_l, src)};
+    return {64 * c + src, __builtin_amdgcn_readlane(n, src),
+            off[c] + (unsigned)__builtin_amdgcn_readlane(excl, src)};
   }
 };
 
@@ -461,8 +503,9 @@ __device__ __forceinline__ u32x4 e5m2_pack16(const u32x4& x0, const u32x4& x1) {
 // of k_new / v_new for sequence b, KV head h) to slot `row` of page
 // page_id. One wave, 16 bytes per lane per row: lane l < 8 encodes K bytes
 // [16l, 16l + 16), lanes 8..15 the V bytes. The same wave later reads the
-// slot with its ordinary loads of the page, which observe its own earlier
-// stores; no other wave reads the slot.
+// slot back with its ordinary loads of the page (other lanes than the ones
+// that stored), so the caller waits for the stores to complete first; no
+// other wave reads the slot.
 __device__ __forceinline__ void append_store(const AttendArgs& a, int b, int h, int page_id, int row,
                                              int lane) {
   if (lane >= 16) return;
@@ -488,6 +531,7 @@ struct SplitShared {
   float m[kWaves][kMaxGroup];
   float l[kWaves][kMaxGroup];
   float o[kWaves][kMaxGroup][kHeadDim + 4];
+  long long chunk_off[kMaxBatch / 64 + 1];   // batches over 64: blocks before each 64-sequence chunk
 };
 
 // One segment of a work item: blocks [jb_lo, jb_hi) of sequence b (n
@@ -567,6 +611,10 @@ __device__ __forceinline__ void append_if_owner(const AttendArgs& a, const Segme
   if (w.t_end == s.n && (s.n < a.max_tokens || a.context_lens[s.b] == s.n) &&
       ((s.n - 1 - w.t_begin) / kBlockTokens) % kWaves == wave) {
     append_store(a, s.b, h, w.bt[(s.n - 1) / kPageSize], (s.n - 1) % kPageSize, lane);
+    // The stores are complete in the L2 cache before the wave issues any K/V
+    // load of the segment: those loads miss the CU's L1 (no wave on this CU
+    // has read the slot's lines in this launch) and read the new bytes.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   }
 }
 
@@ -649,7 +697,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
   const int wave = threadIdx.x >> 6;
   const int Hkv = a.num_kv_heads;
 
-  const SeqTable seqs(context_lens, batch, max_tokens, lane);
+  const SeqTable seqs(context_lens, batch, max_tokens, lane, wave, sh.chunk_off);
   const long long NB = seqs.nb;
   const int P = items_per_head(NB, a.per_head);
   const int item = blockIdx.x / Hkv;
@@ -673,7 +721,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
       }
     }
   }
-  if (item >= P) return;   // the whole workgroup leaves
+  if (item >= P) {   // no work item: the whole workgroup leaves
+    seqs.publish(a.seq_prefix);
+    return;
+  }
   const long long lo = item_lo(item, NB, P);
   const long long hi = item_lo(item + 1, NB, P);
 
@@ -795,6 +846,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
     cw = nw;
     load_q(a, cur, h, lane, qf);
   }
+  seqs.publish(a.seq_prefix);
 }
 
 // ----------------------------------------------------------- combine kernel
@@ -860,7 +912,7 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int32_t* context_
   const int b = bh / Hkv;
   const int h = bh % Hkv;
 
-  const SeqTable seqs(context_lens, batch, max_tokens, lane);
+  const SeqTable seqs(context_lens, batch, max_tokens, lane, a.seq_prefix);
   const long long NB = seqs.nb;
   const int P = items_per_head(NB, a.per_head);
   const SeqInfo sq = seqs.at(b, lane);

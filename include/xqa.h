@@ -232,14 +232,15 @@ xqa_status_t xqa_append_kv(xqa_handle_t handle, const void* k_new, const void* v
                            uint8_t* k_pages, uint8_t* v_pages, void* stream);
 
 /* One serving step in one call: xqa_append_kv followed by xqa_decode, with
- * the append fused into the decode's split kernel. The wave that reads a
- * sequence's last 32-token block encodes the new K and V rows (rounding as
- * for xqa_append_kv), uses them for token n - 1 in place of the loaded bytes
- * and stores them to the page slot, so no separate launch or extra pass is
- * needed. Results (out and the page bytes) equal those of the two calls in
- * sequence. E5M2 cache, one query token. k_pages and v_pages are written
- * (the same contract as xqa_append_kv); other arguments and errors as for
- * xqa_decode and xqa_append_kv. */
+ * the append fused into the decode's split kernel. The wave that will read a
+ * sequence's last 32-token block first encodes the new K and V rows
+ * (rounding as for xqa_append_kv) and stores them to the page slot, waits
+ * until those stores have completed, and only then issues its loads of that
+ * block, which read the new rows back like any cached token; no separate
+ * launch is needed. Results (out and the page bytes) equal those of the two
+ * calls in sequence, bit for bit. E5M2 cache, one query token. k_pages and
+ * v_pages are written (the same contract as xqa_append_kv); other arguments
+ * and errors as for xqa_decode and xqa_append_kv. */
 xqa_status_t xqa_decode_append(xqa_handle_t handle, const void* q, const void* k_new,
                                const void* v_new, uint8_t* k_pages, uint8_t* v_pages,
                                const int32_t* block_table, const int32_t* context_lens,

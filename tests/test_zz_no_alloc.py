@@ -1,5 +1,5 @@
 """xqa_decode_noalloc through the C ABI: the handle-free decode whose split
-states and merge counters live in the library's fixed device array. Its
+states live in the library's fixed device array. Its
 output must equal xqa_decode on a handle made from the same configuration,
 bit for bit, on consecutive calls of different sizes; sizes past the fixed
 array are rejected before anything is launched."""
