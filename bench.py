@@ -89,11 +89,187 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (5x), the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counter readings")
+    ap.add_argument("--calibrate-read", action="store_true",
+                    help="run only a read of a 1 GiB buffer reduced to one value (5x): a second, "
+                         "read-only reference for FETCH_SIZE")
+    ap.add_argument("--abba-rounds", type=int, default=5, help="A/B/B/A rounds per arm pair")
     return ap.parse_args()
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class ClockSampler:
+    """Samples GPU clocks and power in a background thread while timed work runs.
+
+    Reads the driver's sysfs files (current shader / memory clock level and
+    average power) every 20 ms; where they are not readable, rocm-smi (a
+    child process) every 0.5 s. start()/stop() bracket the timed phases.
+    """
+
+    def __init__(self):
+        import glob
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        dev = None
+        for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+            if os.path.exists(os.path.join(d, "pp_dpm_sclk")):
+                dev = d
+                break
+        self.dev = dev
+        self.hwmon = None
+        if dev:
+            hw = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*")))
+            for h in hw:
+                for f in ("power1_average", "power1_input"):
+                    if os.path.exists(os.path.join(h, f)):
+                        self.hwmon = os.path.join(h, f)
+                        break
+        self.source = "sysfs" if dev else "rocm-smi"
+
+    @staticmethod
+    def _level(path):
+        with open(path) as f:
+            for line in f:
+                if "*" in line:
+                    return float(line.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                                 .replace("mhz", ""))
+        return None
+
+    def _read(self):
+        if self.dev:
+            rec = {"sclk_mhz": self._level(os.path.join(self.dev, "pp_dpm_sclk")),
+                   "mclk_mhz": self._level(os.path.join(self.dev, "pp_dpm_mclk"))}
+            if self.hwmon:
+                with open(self.hwmon) as f:
+                    rec["power_w"] = int(f.read().strip()) / 1e6
+            return rec
+        c = gpu_clocks() or {}
+        rec = {}
+        for k, v in c.items():
+            digits = "".join(ch for ch in str(v) if ch.isdigit() or ch == ".")
+            if "sclk" in k and "speed" in k and digits:
+                rec["sclk_mhz"] = float(digits)
+            elif "mclk" in k and "speed" in k and digits:
+                rec["mclk_mhz"] = float(digits)
+            elif "power" in k.lower() and digits:
+                rec["power_w"] = float(digits)
+        return rec
+
+    def _run(self):
+        period = 0.02 if self.dev else 0.5
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                pass
+            self._stop.wait(period)
+
+    def start(self):
+        import threading
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread:
+            self._thread.join(timeout=5)
+        out = {"source": self.source, "samples": len(self.samples)}
+        for key in ("sclk_mhz", "mclk_mhz", "power_w"):
+            vals = [s[key] for s in self.samples if s.get(key) is not None]
+            if vals:
+                out[key] = {"min": min(vals), "median": statistics.median(vals), "max": max(vals)}
+        return out
+
+
+def provenance(args):
+    """Where the numbers come from: sources, build, toolchain, device, inputs."""
+    import hashlib
+    import platform
+    import subprocess
+    import torch
+    from decode_attention_paged_e5m2_amd import build as _build
+
+    def sha(paths):
+        h = hashlib.sha256()
+        for pth in paths:
+            with open(pth, "rb") as f:
+                h.update(f.read())
+        return h.hexdigest()
+
+    pkg = os.path.join(ROOT, "decode_attention_paged_e5m2_amd")
+    csrc = os.path.join(pkg, "csrc")
+    srcs = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    git = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                           timeout=10)
+        if r.returncode == 0:
+            git = r.stdout.strip()
+    except Exception:
+        pass
+    info = {}
+    bi = os.path.join(pkg, "_build_info.json")
+    if os.path.exists(bi):
+        with open(bi) as f:
+            info = json.load(f)
+    rocm = None
+    for cand in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(cand):
+            with open(cand) as f:
+                rocm = f.read().strip()
+            break
+    props = torch.cuda.get_device_properties(0)
+    lib = os.path.join(pkg, "libxqa.so")
+    return {
+        "git_sha": git or info.get("git_sha"),
+        "git_sha_source": "git" if git else ("build info" if info.get("git_sha") else None),
+        "sources_sha256": sha(srcs + [os.path.join(ROOT, "include", "xqa.h")]),
+        "library_sha256": sha([lib]) if os.path.exists(lib) else None,
+        "bench_sha256": sha([os.path.abspath(__file__)]),
+        "build_flags": " ".join(_build.COMMON_FLAGS[:-2]),
+        "build_info": info or None,
+        "rocm_version": rocm,
+        "hip_version": torch.version.hip,
+        "torch_version": torch.__version__,
+        "gpu_name": props.name,
+        "gpu_arch": getattr(props, "gcnArchName", None),
+        "gpu_compute_units": props.multi_processor_count,
+        "host": platform.node(),
+        "seeds": [[1000 + args.config, v] for v in range(args.variants)],
+        "variants": args.variants,
+    }
+
+
+def abba(arms, pair, rounds, block):
+    """A/B/B/A blocks of `block` steps: per arm median and IQR (us per step) and
+    the paired B - A difference per round (B blocks' mean minus A blocks' mean)."""
+    import numpy as np
+    import torch
+    a_name, b_name = pair
+    res = {a_name: [], b_name: []}
+    diffs = []
+    for _ in range(rounds):
+        got = {a_name: [], b_name: []}
+        for arm in (a_name, b_name, b_name, a_name):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            arms[arm](block)
+            torch.cuda.synchronize()
+            got[arm].append((time.perf_counter() - t) / block * 1e6)
+        res[a_name] += got[a_name]
+        res[b_name] += got[b_name]
+        diffs.append(statistics.mean(got[b_name]) - statistics.mean(got[a_name]))
+
+    def summ(v):
+        q1, med, q3 = np.percentile(v, [25, 50, 75])
+        return {"median": float(med), "iqr": [float(q1), float(q3)], "n": len(v)}
+    return {"A": a_name, "B": b_name, "rounds": rounds, "block_steps": block,
+            a_name: summ(res[a_name]), b_name: summ(res[b_name]),
+            "paired_B_minus_A": summ(diffs)}
 
 
 def gpu_clocks():
@@ -194,6 +370,16 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
                           "dispatches": 5}))
+        return 0
+    if args.calibrate_read:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+        res = torch.empty((), dtype=torch.int32, device=dev)
+        for _ in range(5):
+            torch.amax(src, dim=0, out=res)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device read (amax of a 1 GiB int32 buffer)",
+                          "bytes_read": n, "bytes_written": 4, "dispatches": 5}))
         return 0
 
     t0 = time.time()
@@ -302,6 +488,9 @@ def main():
     torch.cuda.synchronize()
     run_multi(max(args.warmup, R))
     torch.cuda.synchronize()
+    sampler = ClockSampler() if read_clocks else None
+    if sampler:
+        sampler.start()
     t_start = time.perf_counter()
     run_multi(steps)
     torch.cuda.synchronize()
@@ -365,20 +554,36 @@ def main():
         log(f"launch floor ({kernels_per_step} empty kernels per step): {us_empty:.2f} us/step")
         detail["floor_us_per_step_empty_kernels"] = us_empty
         del empty_g
+        # The same empty kernels, one step per graph replay: the floor under
+        # the one-step-per-graph arm (the cost of a graph launch per step).
+        empty1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(empty1):
+            for _ in range(kernels_per_step):
+                torch.cuda._sleep(0)
+        for _ in range(max(args.warmup, 2)):
+            empty1.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            empty1.replay()
+        torch.cuda.synchronize()
+        detail["floor_us_per_step_empty_kernels_1step_graph"] = (time.perf_counter() - t) / steps * 1e6
+        del empty1
 
     # ------------------------------------------------------ A/B/B/A blocks
+    # Every arm warmed up on its own above; blocks of the same number of steps
+    # run A B B A, `--abba-rounds` times, for the headline arm against eager
+    # calls and against one step per graph replay. Reported per arm: median and
+    # interquartile range of the blocks; per pair: the paired B - A difference.
     if not args.quick:
-        blk = max(50, min(500, args.steps // 4))
-        res = {"eager": [], "graph": []}
-        for rep in range(3):
-            for arm in ("eager", "graph", "graph", "eager"):
-                torch.cuda.synchronize()
-                t = time.perf_counter()
-                (run_eager if arm == "eager" else run_graph)(blk)
-                torch.cuda.synchronize()
-                res[arm].append((time.perf_counter() - t) / blk * 1e6)
-        detail["abba_us_per_step"] = {k: {"median": statistics.median(v), "min": min(v), "max": max(v)}
-                                      for k, v in res.items()}
+        blk = max(R, min(400, args.steps // 5) // R * R)
+        arms = {"graph_Rstep": run_multi, "eager": run_eager, "graph_1step": run_graph}
+        detail["abba_us_per_step"] = [
+            abba(arms, ("graph_Rstep", "eager"), args.abba_rounds, blk),
+            abba(arms, ("graph_Rstep", "graph_1step"), args.abba_rounds, blk)]
+        for r in detail["abba_us_per_step"]:
+            log(f"A/B/B/A {r['A']} {r[r['A']]['median']:.2f} vs {r['B']} {r[r['B']]['median']:.2f} us/step, "
+                f"paired B-A {r['paired_B_minus_A']['median']:+.2f} us")
         # warm mode: the same variant back to back (may be cache resident)
         torch.cuda.synchronize()
         t = time.perf_counter()
@@ -386,6 +591,8 @@ def main():
             graphs[0].replay()
         torch.cuda.synchronize()
         detail["warm_same_input_us_per_step"] = (time.perf_counter() - t) / blk * 1e6
+    if sampler:
+        detail["gpu_clocks_during_timing"] = sampler.stop()
 
     # --------------------------------------- per-launch timing of each kernel
     # HIP events recorded on the stream the kernels are launched on. A spin
@@ -693,6 +900,7 @@ def main():
             f"fused {us_fused:.2f} us/step")
 
     detail["gpu_clocks_after"] = gpu_clocks() if read_clocks else None
+    prov = provenance(args)
     line = {
         "metric": METRIC,
         "value": gbs,
@@ -716,9 +924,12 @@ def main():
             "pct_of_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
             "us_per_step": us_step,
         },
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic_bytes(args.config)},
+        "roofline": {"bound": "hbm", "kernel": "split_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "step_frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic_bytes(args.config)},
         "cpu_baseline": cpu,
+        "provenance": prov,
         "detail": detail,
     }
     print(json.dumps(line), flush=True)

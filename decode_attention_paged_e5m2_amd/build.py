@@ -54,7 +54,35 @@ def build(verbose: bool = False) -> str:
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
+    write_build_info()
     return LIB_PATH
+
+
+def write_build_info() -> None:
+    """Record what the library was built from next to it (_build_info.json, not
+    versioned): the source commit when git is available, the compiler version
+    and the flags, so that measurements made elsewhere can name their build."""
+    import json
+    import time
+    info = {"built_at_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime()),
+            "flags": " ".join(COMMON_FLAGS[:-2]), "sources": [os.path.basename(x) for x in SOURCES]}
+    try:
+        r = subprocess.run(["git", "-C", REPO_DIR, "rev-parse", "HEAD"], capture_output=True,
+                           text=True, timeout=10)
+        if r.returncode == 0:
+            info["git_sha"] = r.stdout.strip()
+            d = subprocess.run(["git", "-C", REPO_DIR, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=10)
+            info["git_dirty"] = bool(d.stdout.strip())
+    except Exception:
+        pass
+    try:
+        r = subprocess.run([hipcc(), "--version"], capture_output=True, text=True, timeout=60)
+        info["hipcc_version"] = " | ".join(l.strip() for l in r.stdout.splitlines()[:2])
+    except Exception:
+        pass
+    with open(os.path.join(PKG_DIR, "_build_info.json"), "w") as f:
+        json.dump(info, f, indent=1)
 
 
 def resource_usage() -> str:
