@@ -27,14 +27,14 @@ struct Geometry {
   int combine_waves;    // waves per combine workgroup
   bool direct_only;     // no sequence can leave split states: one kernel per step
   size_t partial_bytes; // 2 * grid records
-  size_t prefix_bytes;  // batches over 64: per-chunk block prefix table, after the records
+  size_t desc_bytes;    // merge descriptors: max_batch * Hkv int2, after the records
 };
 
 struct xqa_handle_s {
   xqa_config_t cfg;
   int device;
   Geometry geo;
-  float* partials;    // workspace: 2 * grid split-state records, then the chunk prefix table
+  float* partials;    // workspace: 2 * grid split-state records, then the merge descriptors
   int32_t* vtable;    // page-subset decode: [max_batch][max_selected_pages] page ids, then
   int32_t* vlens;     //   [max_batch] lengths (null when max_selected_pages is 0)
   size_t workspace_bytes;
@@ -99,9 +99,7 @@ xqa::AttendArgs attend_args(const xqa_config_t& cfg, const Geometry& geo, void* 
   a.context_lens = context_lens;
   a.out = static_cast<uint16_t*>(out);
   a.partials = static_cast<float*>(workspace);
-  a.seq_prefix = geo.prefix_bytes > 0
-                     ? reinterpret_cast<long long*>(static_cast<char*>(workspace) + geo.partial_bytes)
-                     : nullptr;
+  a.merge_desc = reinterpret_cast<int2*>(static_cast<char*>(workspace) + geo.partial_bytes);
   a.batch = batch;
   a.num_kv_heads = cfg.num_kv_heads;
   a.group = cfg.num_q_heads / cfg.num_kv_heads;
@@ -112,7 +110,6 @@ xqa::AttendArgs attend_args(const xqa_config_t& cfg, const Geometry& geo, void* 
   a.per_head = geo.per_head;
   a.item_stride = geo.item_stride;
   a.combine_waves = geo.combine_waves;
-  a.zero_empty = geo.direct_only ? 1 : 0;
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.v_scale = 1.0f;
   a.kv_format = xqa::kKvE5M2;
@@ -194,7 +191,7 @@ Geometry geometry(const xqa_config_t& cfg, int cus, int per_cu) {
   g.item_stride = ((G * g.max_q * (xqa::kHeadDim + 2)) + 3) / 4 * 4;
   // Two record slots per work item: its first and its last segment.
   g.partial_bytes = (size_t)2 * g.grid * g.item_stride * sizeof(float);
-  g.prefix_bytes = cfg.max_batch > 64 ? ((size_t)(cfg.max_batch + 63) / 64 + 1) * sizeof(long long) : 0;
+  g.desc_bytes = (size_t)cfg.max_batch * cfg.num_kv_heads * sizeof(int2);
   // A sequence leaves at most one split state per item and per block, so a
   // handle whose bound stays within one combine round gets the one-wave
   // combine workgroups; a longer one shares the rounds over four waves.
@@ -255,7 +252,7 @@ xqa_status_t xqa_create(const xqa_config_t* cfg, xqa_handle_t* out_handle) {
   const size_t vt_elems = cfg->max_selected_pages > 0
                               ? (size_t)cfg->max_batch * cfg->max_selected_pages + cfg->max_batch
                               : 0;
-  const size_t ws = geo.partial_bytes + geo.prefix_bytes;
+  const size_t ws = geo.partial_bytes + geo.desc_bytes;
   h->workspace_bytes = ws + vt_elems * sizeof(int32_t);
   h->partials = nullptr;
   h->vtable = nullptr;
@@ -365,7 +362,7 @@ xqa_status_t xqa_decode_noalloc(const xqa_config_t* cfg, const void* q, const ui
   e = xqa::noalloc_device(dev, &nd);
   if (e != hipSuccess) return hip_fail(e, "fixed workspace lookup");
   const Geometry geo = geometry(*cfg, nd.cus, nd.per_cu);
-  if (geo.partial_bytes + geo.prefix_bytes > xqa::kNoallocScratchBytes)
+  if (geo.partial_bytes + geo.desc_bytes > xqa::kNoallocScratchBytes)
     return fail(XQA_ERR_UNSUPPORTED,
                 "the configuration's split states exceed the fixed 16 MiB workspace "
                 "(fewer max_work_items, KV heads or query rows)");

@@ -75,8 +75,9 @@ struct AttendArgs {
   const int32_t* context_lens;
   uint16_t* out;
   float* partials;        // [2 * grid][item_stride] split states
-  long long* seq_prefix;  // batches over 64: [ceil(batch / 64) + 1] blocks before each 64-sequence
-                          // chunk, written by the split kernel, read by the combine kernel
+  int2* merge_desc;       // [batch][Hkv] {slot of the first state, work item of the last} per
+                          // sequence and KV head ({-1, -1}: no states to merge), written by the
+                          // split kernel, read by the combine kernel
   int32_t batch;
   int32_t num_kv_heads;
   int32_t group;
@@ -87,7 +88,6 @@ struct AttendArgs {
   int32_t per_head;       // grid / Hkv
   int32_t item_stride;    // floats per partial record
   int32_t combine_waves;  // 1: no sequence can leave more than kCombineRound states; else 4
-  int32_t zero_empty;     // no sequence can be split: the split kernel writes the zero rows
   float scale_log2e;      // scale * k_scale * log2(e): scores are kept in base-2 units
   float v_scale;          // per-tensor V dequantisation scale, applied to the normalised rows
   int32_t kv_format;      // KvFormat

@@ -199,12 +199,10 @@ struct SeqInfo {
 // leaves sequence `lane`'s length and block prefix in lane registers, and
 // every later lookup is a v_readlane or a ballot with no memory access.
 // Larger batches keep, per 64-sequence chunk c, the number of blocks before
-// it (off[c], off[nch] = total): the split kernel builds this table once per
-// workgroup in LDS (the four waves share out the chunks, eight chunk loads in
-// flight per wave) and its workgroup 0 copies it to the workspace, where the
-// combine kernel reads it. A lookup is then one load of a chunk's lengths
-// and a scan; finding the chunk that holds a block is a ballot over the
-// table, 64 chunks per step.
+// it (off[c], off[nch] = total), built once per workgroup in LDS (the four
+// waves share out the chunks, eight chunk loads in flight per wave). A lookup
+// is then one load of a chunk's lengths and a scan; finding the chunk that
+// holds a block is a ballot over the table, 64 chunks per step.
 struct SeqTable {
   const int32_t* ctx;
   int batch, max_tokens;
@@ -212,15 +210,17 @@ struct SeqTable {
   int n_l;                  // small: clamped length of sequence `lane` (0 past the batch)
   int excl_l;               // small: first block of sequence `lane`
   int nch;                  // large: 64-sequence chunks
-  const long long* off;     // large: [nch + 1] blocks before each chunk (LDS or global)
+  const long long* off;     // large: [nch + 1] blocks before each chunk (LDS)
+  const int* has_empty;     // large: [nch] nonzero when the chunk holds an empty sequence (LDS)
   long long nb;             // total blocks per head
 
-  // Split kernel: called by every thread of the workgroup (the large path
-  // synchronises the workgroup). lds: room for kMaxBatch / 64 + 1 values;
-  // publish: where workgroup 0 copies the table (may be null).
-  __device__ SeqTable(const int32_t* c, int bt, int mt, int lane, int wave, long long* lds)
+  // Called by every thread of the workgroup (the large path synchronises the
+  // workgroup). lds: room for kMaxBatch / 64 + 1 values; lds_empty: for
+  // kMaxBatch / 64 flags.
+  __device__ SeqTable(const int32_t* c, int bt, int mt, int lane, int wave, long long* lds,
+                      int* lds_empty)
       : ctx(c), batch(bt), max_tokens(mt), small(bt <= 64), n_l(0), excl_l(0), nch(0), off(lds),
-        nb(0) {
+        has_empty(lds_empty), nb(0) {
     if (small) {
       init_small(lane);
       return;
@@ -232,12 +232,17 @@ struct SeqTable {
       for (int k = 0; k < 8; ++k) {   // unconditional (clamped) loads: all eight in flight
         const int i = 64 * (c0 + k) + lane;
         const int n = clamp_len(ctx[min(i, batch - 1)], max_tokens);
-        v[k] = i < batch ? seq_blocks(n) : 0;
+        v[k] = i < batch ? seq_blocks(n) : -1;
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const unsigned tot = (unsigned)__builtin_amdgcn_readlane(wave_inclusive_scan(v[k]), 63);
-        if (lane == 0 && c0 + k < nch) lds[c0 + k] = tot;
+        const bool empty = __ballot(v[k] == 0) != 0;
+        const int blocks = v[k] > 0 ? v[k] : 0;
+        const unsigned tot = (unsigned)__builtin_amdgcn_readlane(wave_inclusive_scan(blocks), 63);
+        if (lane == 0 && c0 + k < nch) {
+          lds[c0 + k] = tot;
+          lds_empty[c0 + k] = empty;
+        }
       }
     }
     __syncthreads();
@@ -256,23 +261,14 @@ struct SeqTable {
     nb = lds[nch];
   }
 
-  // Workgroup 0 of the split kernel copies its table to the workspace for
-  // the combine kernel (batches over 64).
-  __device__ void publish(long long* dst) const {
-    if (small || dst == nullptr || blockIdx.x != 0) return;
-    for (int cc = threadIdx.x; cc <= nch; cc += kThreads) dst[cc] = off[cc];
-  }
-
-  // Combine kernel: the large path reads the table the split kernel published.
-  __device__ SeqTable(const int32_t* c, int bt, int mt, int lane, const long long* published)
-      : ctx(c), batch(bt), max_tokens(mt), small(bt <= 64), n_l(0), excl_l(0), nch(0),
-        off(published), nb(0) {
-    if (small) {
-      init_small(lane);
-    } else {
-      nch = (batch + 63) >> 6;
-      nb = off[nch];
-    }
+  // Sequences with no token among the 64 of chunk c (small: c = 0, from
+  // registers; large: loaded only when the chunk has one).
+  __device__ unsigned long long empty_in_chunk(int c, int lane) const {
+    if (small) return __ballot(lane < batch && n_l == 0);
+    if (!has_empty[c]) return 0;
+    const int i = 64 * c + lane;
+    const int n = clamp_len(ctx[min(i, batch - 1)], max_tokens);
+    return __ballot(i < batch && n == 0);
   }
 
   __device__ void init_small(int lane) {
@@ -532,6 +528,7 @@ struct SplitShared {
   float l[kWaves][kMaxGroup];
   float o[kWaves][kMaxGroup][kHeadDim + 4];
   long long chunk_off[kMaxBatch / 64 + 1];   // batches over 64: blocks before each 64-sequence chunk
+  int chunk_empty[kMaxBatch / 64];           // batches over 64: the chunk holds an empty sequence
 };
 
 // One segment of a work item: blocks [jb_lo, jb_hi) of sequence b (n
@@ -541,6 +538,8 @@ struct SplitShared {
 struct Segment {
   int b, n, jb_lo, jb_hi;
   bool direct;
+  bool first;       // the item's first segment (state slot 2i; a later one uses 2i + 1)
+  long long off;    // the sequence's first block in the head's block stream
   float* rec;
 };
 
@@ -620,9 +619,22 @@ __device__ __forceinline__ void append_if_owner(const AttendArgs& a, const Segme
 
 // The four waves' states of a segment meet in LDS (fixed order); the merged
 // (max, sum, O) is normalised and written, or stored as a split state.
+// The segments at a sequence's ends also fill in its merge descriptor
+// {slot of the first state, item of the last}: the first segment writes the
+// slot, the last one its item; a sequence inside one item writes {-1, -1}.
 __device__ __forceinline__ void finish_segment(const AttendArgs& a, SplitShared& sh,
                                                const Segment& s, const WaveState& st, int h,
-                                               int lane, int wave) {
+                                               int item, int lane, int wave) {
+  if (threadIdx.x == 0) {
+    int2* d = a.merge_desc + (long long)s.b * a.num_kv_heads + h;
+    if (s.direct) {
+      *d = make_int2(-1, -1);
+    } else if (s.jb_lo == 0) {
+      d->x = 2 * item + (s.first ? 0 : 1);
+    } else if (s.jb_hi == seq_blocks(s.n)) {
+      d->y = item;
+    }
+  }
   const int R = a.rows;
   const int g = lane & 15;
   const int q = lane >> 4;
@@ -697,20 +709,22 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
   const int wave = threadIdx.x >> 6;
   const int Hkv = a.num_kv_heads;
 
-  const SeqTable seqs(context_lens, batch, max_tokens, lane, wave, sh.chunk_off);
+  const SeqTable seqs(context_lens, batch, max_tokens, lane, wave, sh.chunk_off, sh.chunk_empty);
   const long long NB = seqs.nb;
   const int P = items_per_head(NB, a.per_head);
   const int item = blockIdx.x / Hkv;
   const int h = blockIdx.x % Hkv;
-  if (a.zero_empty) {
-    // No combine runs on this handle: the zero rows of empty sequences are
-    // written here. Wave w of item i takes the 64-sequence chunks
-    // 4i + w, 4i + w + 4 per_head, ...; each empty sequence's R rows are
-    // written by the whole wave, 16 bytes per lane per store.
+  // Empty sequences: zero rows and a merge descriptor with no states,
+  // written once the workgroup's own work is done. Wave w of item i takes
+  // the 64-sequence chunks 4i + w, 4i + w + 4 per_head, ...; each empty
+  // sequence's R rows are written by the whole wave, 16 bytes per lane per
+  // store.
+  auto finish_empty = [&]() {
     const int R = a.rows;
     for (int b0 = 64 * (kWaves * item + wave); b0 < a.batch; b0 += 64 * kWaves * a.per_head) {
       const int bl = b0 + lane;
-      unsigned long long empty = __ballot(bl < a.batch && clamp_len(a.context_lens[bl], a.max_tokens) == 0);
+      unsigned long long empty = seqs.empty_in_chunk(b0 >> 6, lane);
+      if ((empty >> lane) & 1) a.merge_desc[(long long)bl * Hkv + h] = make_int2(-1, -1);
       while (empty) {
         const int bz = b0 + __ffsll(empty) - 1;
         empty &= empty - 1;
@@ -720,9 +734,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
         }
       }
     }
-  }
+  };
   if (item >= P) {   // no work item: the whole workgroup leaves
-    seqs.publish(a.seq_prefix);
+    finish_empty();
     return;
   }
   const long long lo = item_lo(item, NB, P);
@@ -761,6 +775,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
     // Items are contiguous block ranges, so the sequence lies in one item
     // exactly when all its blocks fall in this item's range [lo, hi).
     s.direct = sq.off >= lo && sq.off + nb <= hi;
+    s.first = first;
+    s.off = sq.off;
     s.rec = a.partials + ((long long)(2 * item + (first ? 0 : 1)) * Hkv + h) * a.item_stride;
     return s;
   };
@@ -839,17 +855,19 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
       if constexpr (kAppend) append_if_owner(a, nxt, nw, h, lane, wave);
       issue(A, ids, 0);
     }
-    finish_segment(a, sh, cur, st, h, lane, wave);
+    finish_segment(a, sh, cur, st, h, item, lane, wave);
     if (!has_next) break;
     sq = nq;
     cur = nxt;
     cw = nw;
     load_q(a, cur, h, lane, qf);
   }
-  seqs.publish(a.seq_prefix);
+  finish_empty();
 }
 
 // ----------------------------------------------------------- combine kernel
+// The combine kernel needs neither the lengths nor the plan: it reads the
+// merge descriptor the split kernel wrote for its (sequence, KV head).
 // Workgroups of W waves (W = 1, or 4 when a sequence can leave more states
 // than one round holds) merge each sequence's split states with the
 // log-sum-exp rule, reading states in rounds of kCombineRound with every load
@@ -899,35 +917,30 @@ struct CombineShared {
 };
 
 template <int W>
-__global__ __launch_bounds__(64 * W) void combine_kernel(const int32_t* context_lens, int32_t batch,
-                                                         int32_t max_tokens, AttendArgs a) {
+__global__ __launch_bounds__(64 * W) void combine_kernel(const int2* merge_desc, int32_t hkv,
+                                                         AttendArgs a) {
   constexpr int kWgCols = 16 * W;
   constexpr int kChunks = kHeadDim / kWgCols;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int R = a.rows;
-  const int Hkv = a.num_kv_heads;
+  const int Hkv = hkv;
   const int chunk = blockIdx.x % kChunks;
   const int bh = blockIdx.x / kChunks;
   const int b = bh / Hkv;
   const int h = bh % Hkv;
 
-  const SeqTable seqs(context_lens, batch, max_tokens, lane, a.seq_prefix);
-  const long long NB = seqs.nb;
-  const int P = items_per_head(NB, a.per_head);
-  const SeqInfo sq = seqs.at(b, lane);
-  if (sq.n == 0) {
-    for (int e = threadIdx.x; e < R * (kWgCols / 2); e += 64 * W) {
-      *(uint32_t*)(out_row(a, b, h, e / (kWgCols / 2)) + chunk * kWgCols + (e % (kWgCols / 2)) * 2) = 0;
-    }
-    return;
-  }
-  const int i0 = item_of_block(sq.off, NB, P);
-  const int nsb = item_of_block(sq.off + seq_blocks(sq.n) - 1, NB, P) - i0 + 1;
-  if (nsb == 1) return;   // written by the split kernel
-  // Item i0 holds this sequence in slot 2*i0 if the sequence starts its
-  // block range, else in slot 2*i0 + 1; later items hold it in slot 2*i.
-  const int slot0 = (sq.off == item_lo(i0, NB, P)) ? 2 * i0 : 2 * i0 + 1;
+  // The split kernel's record of this (sequence, KV head): the slot of its
+  // first state and the work item of its last. Empty sequences and
+  // sequences finished in one work item (slot -1) were written by the split
+  // kernel.
+  const int2 desc = merge_desc[bh];
+  const int slot0 = desc.x;
+  if (slot0 < 0) return;
+  // The first state is in slot 2 i0 (the sequence starts item i0's block
+  // range) or 2 i0 + 1; later items i hold it in slot 2 i.
+  const int i0 = slot0 >> 1;
+  const int nsb = desc.y - i0 + 1;
   const int mo = R * kHeadDim;
   auto rec = [&](int s) {
     const int slot = s == 0 ? slot0 : 2 * (i0 + s);
@@ -1091,12 +1104,12 @@ hipError_t launch_combine(const AttendArgs& a, hipStream_t stream) {
   if (a.combine_waves == kCombineMaxWaves) {
     constexpr int W = kCombineMaxWaves;
     const int grid = a.batch * a.num_kv_heads * (kHeadDim / (16 * W));
-    hipLaunchKernelGGL(combine_kernel<W>, dim3(grid), dim3(64 * W), 0, stream, a.context_lens,
-                       a.batch, a.max_tokens, a);
+    hipLaunchKernelGGL(combine_kernel<W>, dim3(grid), dim3(64 * W), 0, stream, a.merge_desc,
+                       a.num_kv_heads, a);
   } else {
     const int grid = a.batch * a.num_kv_heads * (kHeadDim / 16);
-    hipLaunchKernelGGL(combine_kernel<1>, dim3(grid), dim3(64), 0, stream, a.context_lens,
-                       a.batch, a.max_tokens, a);
+    hipLaunchKernelGGL(combine_kernel<1>, dim3(grid), dim3(64), 0, stream, a.merge_desc,
+                       a.num_kv_heads, a);
   }
   return hipGetLastError();
 }

@@ -132,9 +132,10 @@ xqa_status_t xqa_decode(xqa_handle_t handle, const void* q, const uint8_t* k_pag
 
 /* xqa_decode without a handle, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
- * forbid hipMalloc. The split-state records live in a fixed 16 MiB device
- * array inside the library (one per GPU, held until the process ends)
- * instead of a handle's workspace; nothing is allocated, here or later. cfg
+ * forbid hipMalloc. The split-state records and the per-(sequence, KV head)
+ * merge records live in a fixed 16 MiB device array inside the library (one
+ * per GPU, held until the process ends) instead of a handle's workspace;
+ * nothing is allocated, here or later. cfg
  * (host memory) is validated as by xqa_create and sizes the step exactly as
  * a handle made from it would, so the output is bitwise that of xqa_decode
  * on such a handle. The first call on a device looks up the array's address
@@ -143,8 +144,9 @@ xqa_status_t xqa_decode(xqa_handle_t handle, const void* q, const uint8_t* k_pag
  * and safe; calls that overlap in time on one GPU (other streams, other
  * threads) race and give undefined results. Nothing in the array needs to
  * start at zero: every record a call reads, the same call wrote. Limit:
- * 2 * split grid * record floats * 4 bytes must fit 16 MiB (the default
- * grid on one MI355X does for every supported head shape). Arguments,
+ * 2 * split grid * record floats * 4 bytes plus max_batch * Hkv * 8 bytes
+ * must fit 16 MiB (the default grid on one MI355X does for every supported
+ * head shape up to max_batch 65536 with 8 KV heads). Arguments,
  * alignment and errors as for xqa_decode, with cfg's max_batch;
  * INVALID_ARG / UNSUPPORTED as for xqa_create; UNSUPPORTED also when the
  * records do not fit the fixed array. */
@@ -189,20 +191,22 @@ xqa_status_t xqa_decode_fp8(xqa_handle_t handle, xqa_kv_format_t kv_format, cons
                             void* out, void* stream);
 
 /* First stage of xqa_decode alone (device-side plan, page gather, widening,
- * QK, online softmax, PV): rows of sequences that fit one work item are
- * written to out; the others leave split states in the workspace. Same
- * arguments and errors as xqa_decode. xqa_decode_combine must follow on the
- * same stream, with the same context_lens, batch and out, before the handle
- * is used again. Exposed so the two stages can be timed or scheduled apart.
- * On a handle with kernels_per_step 1 the split kernel also writes the zero
- * rows, and the combine finds nothing left to do. */
+ * QK, online softmax, PV): rows of sequences that fit one work item and the
+ * zero rows of sequences with n <= 0 are written to out; the other
+ * sequences leave split states in the workspace, with a per-(sequence, KV
+ * head) record of where they are. Same arguments and errors as xqa_decode.
+ * xqa_decode_combine must follow on the same stream, with the same batch and
+ * out, before the handle is used again. Exposed so the two stages can be
+ * timed or scheduled apart. On a handle with kernels_per_step 1 no sequence
+ * is split, and the combine finds nothing left to do. */
 xqa_status_t xqa_decode_split(xqa_handle_t handle, const void* q, const uint8_t* k_pages,
                               const uint8_t* v_pages, const int32_t* block_table,
                               const int32_t* context_lens, int32_t batch, float scale,
                               void* out, void* stream);
 
 /* Second stage of xqa_decode alone: log-sum-exp merge of the split states of
- * every long sequence (fixed order) and zero rows for sequences with n <= 0.
+ * every sequence the split stage left split (fixed order), found through the
+ * records the split stage wrote; context_lens is checked but not read.
  * Errors: INVALID_ARG (null or misaligned pointers, batch out of range), HIP. */
 xqa_status_t xqa_decode_combine(xqa_handle_t handle, const int32_t* context_lens,
                                 int32_t batch, void* out, void* stream);

@@ -155,8 +155,10 @@ int main() {
   EXPECT(xqa_get_info(h, &info) == XQA_OK);
   EXPECT(info.max_work_items == 512 && info.items_per_head == 128);
   EXPECT(info.kernels_per_step == 2);
-  EXPECT(info.workspace_bytes ==
-         (int64_t)2 * 512 * info.item_stride_floats * 4 + (int64_t)(16 * 16384 + 16) * 4);
+  // split-state records, merge descriptors (16 sequences x 4 heads x 8 bytes),
+  // then the page-subset table
+  EXPECT(info.workspace_bytes == (int64_t)2 * 512 * info.item_stride_floats * 4 + 16 * 4 * 8 +
+                                     (int64_t)(16 * 16384 + 16) * 4);
   EXPECT(info.item_stride_floats % 4 == 0 && info.item_stride_floats >= 8 * 130);
 
   g_launches.clear();
@@ -169,7 +171,8 @@ int main() {
     EXPECT(a.max_pages == 16384 && a.max_tokens == 16384 * 16 && a.per_head == 128);
     EXPECT(a.k_new == nullptr && a.v_new == nullptr && a.kv_format == xqa::kKvE5M2);
     EXPECT(std::fabs(a.scale_log2e - 0.0883883f * 1.4426950408889634f) < 1e-7f);
-    EXPECT(a.v_scale == 1.0f && a.zero_empty == 0);
+    EXPECT(a.v_scale == 1.0f);
+    EXPECT((const char*)a.merge_desc == (const char*)a.partials + (size_t)2 * 512 * info.item_stride_floats * 4);
   }
 
   // Rejected calls launch nothing.
@@ -247,7 +250,7 @@ int main() {
   EXPECT(xqa_get_info(h, &info) == XQA_OK && info.kernels_per_step == 1);
   g_launches.clear();
   EXPECT(xqa_decode(h, p16, kv, kv, i32, i32, 100, 0.1f, p16, nullptr) == XQA_OK);
-  EXPECT(g_launches.size() == 1 && g_launches[0].a.zero_empty == 1);
+  EXPECT(g_launches.size() == 1);
   EXPECT(xqa_decode_pages(h, p16, kv, kv, i32, i32, i32, i32, 1, 4, 0.1f, p16, nullptr) ==
          XQA_ERR_UNSUPPORTED);
   EXPECT(xqa_destroy(h) == XQA_OK);
@@ -291,7 +294,7 @@ int main() {
     // A handle-free call on a one-kernel configuration launches one kernel.
     xqa_config_t one = config(100, 16, 2, 2);
     EXPECT(xqa_decode_noalloc(&one, p16, kv, kv, i32, i32, 100, 0.1f, p16, nullptr) == XQA_OK);
-    EXPECT(g_launches.size() == 1 && g_launches[0].a.zero_empty == 1);
+    EXPECT(g_launches.size() == 1);
     EXPECT(xqa::g_noalloc_lookups > 0);
   }
 
