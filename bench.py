@@ -185,8 +185,16 @@ class ClockSampler:
         return out
 
 
-def provenance(args):
-    """Where the numbers come from: sources, build, toolchain, device, inputs."""
+def under_profiler():
+    """True when a profiler's library is preloaded into this process."""
+    pre = os.environ.get("LD_PRELOAD", "") + os.environ.get("HSA_TOOLS_LIB", "")
+    return "rocprof" in pre or any(k.startswith("ROCPROF") for k in os.environ)
+
+
+def provenance(args, run_git=True):
+    """Where the numbers come from: sources, build, toolchain, device, inputs.
+    run_git: ask git for the commit (a child process); otherwise the build's
+    record of it is used."""
     import hashlib
     import platform
     import subprocess
@@ -204,13 +212,14 @@ def provenance(args):
     csrc = os.path.join(pkg, "csrc")
     srcs = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
     git = None
-    try:
-        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
-                           timeout=10)
-        if r.returncode == 0:
-            git = r.stdout.strip()
-    except Exception:
-        pass
+    if run_git:
+        try:
+            r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                               text=True, timeout=10)
+            if r.returncode == 0:
+                git = r.stdout.strip()
+        except Exception:
+            pass
     info = {}
     bi = os.path.join(pkg, "_build_info.json")
     if os.path.exists(bi):
@@ -348,8 +357,11 @@ def main():
     import numpy as np
     import torch
 
-    # Profiling runs (--no-extras, --calibrate-copy) start no child process.
-    read_clocks = not (args.no_extras or args.calibrate_copy)
+    # Profiling runs (--no-extras, the calibrations, or any run under
+    # rocprofv3, whose preloaded library would also load into a child and
+    # initialise the GPU there) start no child process.
+    read_clocks = not (args.no_extras or args.calibrate_copy or args.calibrate_read
+                       or under_profiler())
     clocks_before = gpu_clocks() if read_clocks else None
     from decode_attention_paged_e5m2_amd import Xqa
     from workloads import make_config
@@ -900,7 +912,7 @@ def main():
             f"fused {us_fused:.2f} us/step")
 
     detail["gpu_clocks_after"] = gpu_clocks() if read_clocks else None
-    prov = provenance(args)
+    prov = provenance(args, run_git=read_clocks)
     line = {
         "metric": METRIC,
         "value": gbs,

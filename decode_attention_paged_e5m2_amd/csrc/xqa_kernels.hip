@@ -213,14 +213,15 @@ struct SeqTable {
   const long long* off;     // large: [nch + 1] blocks before each chunk (LDS)
   const int* has_empty;     // large: [nch] nonzero when the chunk holds an empty sequence (LDS)
   long long nb;             // total blocks per head
+  bool any_empty;           // some sequence of the batch has no token
 
   // Called by every thread of the workgroup (the large path synchronises the
   // workgroup). lds: room for kMaxBatch / 64 + 1 values; lds_empty: for
-  // kMaxBatch / 64 flags.
+  // kMaxBatch / 64 + 1 flags (the last one: any chunk has one).
   __device__ SeqTable(const int32_t* c, int bt, int mt, int lane, int wave, long long* lds,
                       int* lds_empty)
       : ctx(c), batch(bt), max_tokens(mt), small(bt <= 64), n_l(0), excl_l(0), nch(0), off(lds),
-        has_empty(lds_empty), nb(0) {
+        has_empty(lds_empty), nb(0), any_empty(false) {
     if (small) {
       init_small(lane);
       return;
@@ -248,27 +249,37 @@ struct SeqTable {
     __syncthreads();
     if (wave == 0) {
       long long run = 0;
+      bool any = false;
       for (int c0 = 0; c0 < nch; c0 += 64) {
         const int cc = c0 + lane;
         const unsigned t = cc < nch ? (unsigned)lds[cc] : 0u;
+        const bool chunk_any = __ballot(cc < nch && lds_empty[cc] != 0) != 0;
+        any = any | chunk_any;
         const unsigned incl = (unsigned)wave_inclusive_scan((int)t);
         if (cc < nch) lds[cc] = run + incl - t;
         run += (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
       }
-      if (lane == 0) lds[nch] = run;
+      if (lane == 0) {
+        lds[nch] = run;
+        lds_empty[nch] = any;
+      }
     }
     __syncthreads();
     nb = lds[nch];
+    any_empty = lds_empty[nch] != 0;
   }
 
-  // Sequences with no token among the 64 of chunk c (small: c = 0, from
-  // registers; large: loaded only when the chunk has one).
-  __device__ unsigned long long empty_in_chunk(int c, int lane) const {
-    if (small) return __ballot(lane < batch && n_l == 0);
-    if (!has_empty[c]) return 0;
-    const int i = 64 * c + lane;
-    const int n = clamp_len(ctx[min(i, batch - 1)], max_tokens);
-    return __ballot(i < batch && n == 0);
+  // Whether sequence b (this lane's; b < batch when in_batch) has no token.
+  // Every lane of the wave calls it. Small: the length is read from lane
+  // b's registers by a cross-lane read that every lane executes (a lane
+  // left out of it would return no value); large: loaded only when b's
+  // chunk holds an empty sequence.
+  __device__ bool is_empty(int b, bool in_batch) const {
+    if (small) {
+      const int n = __shfl(n_l, b & 63);
+      return in_batch && n == 0;
+    }
+    return in_batch && has_empty[b >> 6] && clamp_len(ctx[b], max_tokens) == 0;
   }
 
   __device__ void init_small(int lane) {
@@ -277,6 +288,7 @@ struct SeqTable {
     const int incl = wave_inclusive_scan(b_l);   // <= 64 * 2^19: no overflow
     excl_l = incl - b_l;
     nb = __builtin_amdgcn_readlane(incl, 63);
+    any_empty = __ballot(lane < batch && n_l == 0) != 0;
   }
 
   // One 64-sequence chunk: lane's length and its block offset inside the chunk.
@@ -528,7 +540,8 @@ struct SplitShared {
   float l[kWaves][kMaxGroup];
   float o[kWaves][kMaxGroup][kHeadDim + 4];
   long long chunk_off[kMaxBatch / 64 + 1];   // batches over 64: blocks before each 64-sequence chunk
-  int chunk_empty[kMaxBatch / 64];           // batches over 64: the chunk holds an empty sequence
+  int chunk_empty[kMaxBatch / 64 + 1];       // batches over 64: the chunk holds an empty sequence;
+                                             // last used entry: any chunk does
 };
 
 // One segment of a work item: blocks [jb_lo, jb_hi) of sequence b (n
@@ -714,20 +727,24 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
   const int P = items_per_head(NB, a.per_head);
   const int item = blockIdx.x / Hkv;
   const int h = blockIdx.x % Hkv;
-  // Empty sequences: zero rows and a merge descriptor with no states,
-  // written once the workgroup's own work is done. Wave w of item i takes
-  // the 64-sequence chunks 4i + w, 4i + w + 4 per_head, ...; each empty
-  // sequence's R rows are written by the whole wave, 16 bytes per lane per
-  // store.
+  // Empty sequences: zero rows and a merge record with no states, written
+  // once the workgroup's own work is done. Sequence b belongs to item
+  // b % per_head, wave (b / per_head) % 4, so the writes spread over the
+  // grid; each empty sequence's R rows are written by its whole wave, 16
+  // bytes per lane per store.
   auto finish_empty = [&]() {
+    if (!seqs.any_empty) return;
     const int R = a.rows;
-    for (int b0 = 64 * (kWaves * item + wave); b0 < a.batch; b0 += 64 * kWaves * a.per_head) {
-      const int bl = b0 + lane;
-      unsigned long long empty = seqs.empty_in_chunk(b0 >> 6, lane);
-      if ((empty >> lane) & 1) a.merge_desc[(long long)bl * Hkv + h] = make_int2(-1, -1);
-      while (empty) {
-        const int bz = b0 + __ffsll(empty) - 1;
-        empty &= empty - 1;
+    const long long ph = a.per_head;
+    // Lane l of wave w looks at k = w + 4 (l + 64 j), sequence item + k per_head.
+    for (long long kb = wave; item + kb * ph < a.batch; kb += kWaves * 64) {
+      const long long bl = item + (kb + kWaves * lane) * ph;
+      const bool empty = seqs.is_empty((int)min(bl, (long long)a.batch - 1), bl < a.batch);
+      unsigned long long mask = __ballot(empty);
+      if (empty) a.merge_desc[bl * Hkv + h] = make_int2(-1, -1);
+      while (mask) {
+        const int bz = (int)(item + (kb + kWaves * (__ffsll(mask) - 1)) * ph);
+        mask &= mask - 1;
         for (int e = lane; e < R * (kHeadDim / 8); e += 64) {
           *(uint4*)(out_row(a, bz, h, e / (kHeadDim / 8)) + (e % (kHeadDim / 8)) * 8) =
               make_uint4(0, 0, 0, 0);
@@ -918,7 +935,7 @@ struct CombineShared {
 
 template <int W>
 __global__ __launch_bounds__(64 * W) void combine_kernel(const int2* merge_desc, int32_t hkv,
-                                                         AttendArgs a) {
+                                                         int32_t per_head, AttendArgs a) {
   constexpr int kWgCols = 16 * W;
   constexpr int kChunks = kHeadDim / kWgCols;
   const int lane = threadIdx.x & 63;
@@ -936,10 +953,12 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int2* merge_desc,
   // kernel.
   const int2 desc = merge_desc[bh];
   const int slot0 = desc.x;
-  if (slot0 < 0) return;
   // The first state is in slot 2 i0 (the sequence starts item i0's block
-  // range) or 2 i0 + 1; later items i hold it in slot 2 i.
+  // range) or 2 i0 + 1; later items i hold it in slot 2 i. A record that
+  // does not describe at least two states inside the grid's slots is not
+  // read (a valid one always does).
   const int i0 = slot0 >> 1;
+  if (slot0 < 0 || desc.y <= i0 || desc.y >= per_head) return;
   const int nsb = desc.y - i0 + 1;
   const int mo = R * kHeadDim;
   auto rec = [&](int s) {
@@ -1105,11 +1124,11 @@ hipError_t launch_combine(const AttendArgs& a, hipStream_t stream) {
     constexpr int W = kCombineMaxWaves;
     const int grid = a.batch * a.num_kv_heads * (kHeadDim / (16 * W));
     hipLaunchKernelGGL(combine_kernel<W>, dim3(grid), dim3(64 * W), 0, stream, a.merge_desc,
-                       a.num_kv_heads, a);
+                       a.num_kv_heads, a.per_head, a);
   } else {
     const int grid = a.batch * a.num_kv_heads * (kHeadDim / 16);
     hipLaunchKernelGGL(combine_kernel<1>, dim3(grid), dim3(64), 0, stream, a.merge_desc,
-                       a.num_kv_heads, a);
+                       a.num_kv_heads, a.per_head, a);
   }
   return hipGetLastError();
 }
