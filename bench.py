@@ -44,9 +44,9 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE x2.00, WRITE_SIZE x1.00). Valid only for the kernel sources
 # whose hash is recorded; any change to them reports null until re-measured.
 MEASURED_TRAFFIC = {
-    "sources_sha256": "f35b0e0cab10740a59e44e5aa33a14def29af1b76c813a0492b93769f87d6216",
-    "fetch_kib": 133343.9, "fetch_scale": 2.0,
-    "write_kib": 2323.8, "write_scale": 1.0,
+    "sources_sha256": "89266a797ee520f32f73386927cef655fc213be3e9bbddf02c97cce80c5babb7",
+    "fetch_kib": 133379.4, "fetch_scale": 2.0,
+    "write_kib": 2328.0, "write_scale": 1.0,
 }
 
 
@@ -525,49 +525,57 @@ def main():
               "gpu_clocks_before": clocks_before}
 
     if not args.no_extras:
-        # Floor: the same R-step graph with every context length 0 (launches,
-        # plan, zero rows), the fixed cost under each step.
+        # Floors. A replay of a graph costs the host ~15-20 us whatever the
+        # graph holds, so a graph of a few near-empty steps measures the
+        # host, not the GPU: the floors use graphs of FLOOR_STEPS steps, long
+        # enough that the GPU's work per replay exceeds the host's launch.
+        FLOOR_STEPS = 32
+        floor_reps = max(steps // FLOOR_STEPS, 8)
+        # Zero lengths: the decode graph's kernels with every context length 0
+        # (launches, plan, zero rows), the fixed cost under each step.
         zero_lens = [torch.zeros_like(d.context_lens) for d in devs]
         zero_outs = [torch.empty_like(d.q) for d in devs]
         floor_g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(floor_g):
-            for d, z, o in zip(devs, zero_lens, zero_outs):
+            for k in range(FLOOR_STEPS):
+                d, z, o = devs[k % R], zero_lens[k % R], zero_outs[k % R]
                 xqa.decode(q=d.q, k_pages=d.k_pages, v_pages=d.v_pages, block_table=d.block_table,
                            context_lens=z, scale=w0.scale, out=o)
-        for _ in range(max(args.warmup // R, 2)):
+        for _ in range(4):
             floor_g.replay()
         torch.cuda.synchronize()
         t = time.perf_counter()
-        for _ in range(steps // R):
+        for _ in range(floor_reps):
             floor_g.replay()
         torch.cuda.synchronize()
-        us_floor = (time.perf_counter() - t) / steps * 1e6
+        us_floor = (time.perf_counter() - t) / (floor_reps * FLOOR_STEPS) * 1e6
         if not all(bool((o == 0).all()) for o in zero_outs):
             print(json.dumps({"error": "zero-length step did not write zero rows"}))
             return 1
-        log(f"floor (all lengths 0, same graph shape): {us_floor:.2f} us/step")
+        log(f"floor (all lengths 0, graph of {FLOOR_STEPS} steps): {us_floor:.2f} us/step")
         detail["floor_us_per_step_zero_lengths"] = us_floor
+        detail["floor_graph_steps"] = FLOOR_STEPS
         del floor_g
-        # Launch floor: a graph of as many empty kernels (a zero-cycle spin)
-        # as the decode graph has launches, replayed the same way.
+        # Launch floor: as many empty kernels (a zero-cycle spin, one
+        # workgroup) per step as the decode step launches, same graph length.
         kernels_per_step = int(info.get("kernels_per_step", 2))
         empty_g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(empty_g):
-            for _ in range(R * kernels_per_step):
+            for _ in range(FLOOR_STEPS * kernels_per_step):
                 torch.cuda._sleep(0)
-        for _ in range(max(args.warmup // R, 2)):
+        for _ in range(4):
             empty_g.replay()
         torch.cuda.synchronize()
         t = time.perf_counter()
-        for _ in range(steps // R):
+        for _ in range(floor_reps):
             empty_g.replay()
         torch.cuda.synchronize()
-        us_empty = (time.perf_counter() - t) / steps * 1e6
+        us_empty = (time.perf_counter() - t) / (floor_reps * FLOOR_STEPS) * 1e6
         log(f"launch floor ({kernels_per_step} empty kernels per step): {us_empty:.2f} us/step")
         detail["floor_us_per_step_empty_kernels"] = us_empty
         del empty_g
-        # The same empty kernels, one step per graph replay: the floor under
-        # the one-step-per-graph arm (the cost of a graph launch per step).
+        # The same empty kernels, one step per graph replay: bounded by the
+        # host's launch of a graph, the floor under the one-step-per-graph arm.
         empty1 = torch.cuda.CUDAGraph()
         with torch.cuda.graph(empty1):
             for _ in range(kernels_per_step):
@@ -680,15 +688,17 @@ def main():
     # write back), which streams through the L2 caches and the 256 MiB
     # on-package cache: the step reads its KV bytes from HBM even when they
     # would fit on package.
-    # Warm: the same variant's step repeated with nothing in between. Both
-    # carry the same event-pair overhead (~2 us), so their difference is the
-    # cache effect alone.
+    # Warm: the same variant's step repeated with nothing in between.
+    # Rotating: the variants in turn with nothing in between, as in the
+    # headline graph but one step per replay. All three carry the same
+    # event-pair overhead and the same per-replay graph launch, so cold minus
+    # rotating is the cost of starting from flushed caches.
     if not args.quick:
         flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         flush_out = torch.empty((), dtype=torch.uint8, device=dev)
         n_cold = max(20, min(100, args.steps // 20))
 
-        def event_steps(flush):
+        def event_steps(flush, rotate):
             pairs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
                      for _ in range(n_cold)]
 
@@ -697,19 +707,21 @@ def main():
                     if flush:
                         torch.amax(flush_buf, dim=0, out=flush_out)
                     pairs[k][0].record(stream)
-                    graphs[k % R if flush else 0].replay()
+                    graphs[k % R if rotate else 0].replay()
                     pairs[k][1].record(stream)
 
             ok = queued_behind_spin(enqueue)
             return ok, statistics.median(a.elapsed_time(b) * 1e3 for a, b in pairs)
 
-        ok_c, cold_us = event_steps(True)
-        ok_w, warm_us = event_steps(False)
+        ok_c, cold_us = event_steps(True, True)
+        ok_r, rot_us = event_steps(False, True)
+        ok_w, warm_us = event_steps(False, False)
         detail["cold_vs_warm_event_pair_us_per_step"] = {
-            "cold_flushed_median": cold_us, "warm_same_input_median": warm_us,
-            "steps": n_cold, "queued_behind_spin": ok_c and ok_w}
+            "cold_flushed_median": cold_us, "rotating_median": rot_us,
+            "warm_same_input_median": warm_us, "steps": n_cold,
+            "queued_behind_spin": ok_c and ok_r and ok_w}
         log(f"one step per event pair: cold (1 GiB read before each) {cold_us:.2f} us, "
-            f"warm (same input repeated) {warm_us:.2f} us")
+            f"rotating variants {rot_us:.2f} us, warm (same input repeated) {warm_us:.2f} us")
         del flush_buf, flush_out
 
     # ------------------------------------------------- multi-token decode

@@ -40,7 +40,8 @@ def test_counter_summary_matches_bench_constants():
 def test_trace_summaries_name_the_measured_sources():
     h = bench.MEASURED_TRAFFIC["sources_sha256"]
     for name in ("split_kernel_ragged_b16_kernel_trace.md", "all_workloads_kernel_trace.md",
-                 "next_rows_ragged_b16_kernel_trace.md"):
+                 "next_rows_ragged_b16_kernel_trace.md",
+                 "split_and_combine_uniform_b8_boundary_b16_counters.md"):
         assert _hash(_read(name)) == h, name
 
 
