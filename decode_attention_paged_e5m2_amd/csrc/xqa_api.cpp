@@ -520,10 +520,34 @@ xqa_status_t xqa_plan(xqa_handle_t h, const int32_t* ctx, int32_t batch, int32_t
   if (batch < 1 || batch > h->cfg.max_batch)
     return fail(XQA_ERR_INVALID_ARG, "batch outside [1, max_batch]");
   const int max_tokens = h->cfg.max_pages_per_seq * xqa::kPageSize;
-  long long nb_total = 0;
+  long long nb_total = 0, cost_total = 0;
   for (int b = 0; b < batch; ++b) nb_total += xqa::seq_blocks(xqa::clamp_len(ctx[b], max_tokens));
   const int P = xqa::items_per_head(nb_total, h->geo.per_head);
-  *split_tokens = P > 0 ? (int32_t)((nb_total + P - 1) / P * xqa::kBlockTokens) : 0;
+  for (int b = 0; b < batch; ++b)
+    cost_total += xqa::seq_cost(xqa::seq_blocks(xqa::clamp_len(ctx[b], max_tokens)), nb_total, P);
+  // Walk the cost stream once: each item's end, as a block.
+  long long largest = 0, lo = 0, coff = 0, off = 0;
+  int b = 0;
+  for (int i = 1; i <= P; ++i) {
+    const long long c = xqa::item_lo(i, cost_total, P);
+    long long hi = nb_total;
+    if (c < cost_total) {
+      for (;; ++b) {
+        const int blocks = xqa::seq_blocks(xqa::clamp_len(ctx[b], max_tokens));
+        const int cost = xqa::seq_cost(blocks, nb_total, P);
+        if (c < coff + cost) {
+          const long long local = c - coff - (cost - blocks);
+          hi = off + (local > 0 ? local : 0);
+          break;
+        }
+        coff += cost;
+        off += blocks;
+      }
+    }
+    largest = std::max(largest, hi - lo);
+    lo = hi;
+  }
+  *split_tokens = (int32_t)(largest * xqa::kBlockTokens);
   *num_items = P * h->cfg.num_kv_heads;
   return XQA_OK;
 }

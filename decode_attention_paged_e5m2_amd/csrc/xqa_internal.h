@@ -32,10 +32,25 @@ constexpr int kCombineMaxWaves = 4;                    // waves per combine work
 //   nb_b  = ceil(n_b / 32)              32-token blocks of sequence b
 //   off_b = sum_{b' < b} nb_b'          first block of b in the head's block stream
 //   NB    = sum_b nb_b
-//   P     = min(per_head, ceil(NB / 8))  work items (each at least 8 blocks)
-//   item i covers blocks [lo_i, lo_{i+1}) with lo_i = floor(i * NB / P), so
-//   every item holds floor(NB / P) or ceil(NB / P) blocks and every CU gets
-//   the same amount of KV bytes. Block x lies in item ceil((x + 1) P / NB) - 1.
+//   P     = min(per_head, ceil(NB / 8))  work items
+//
+// Items are cut by cost, not by blocks alone. Starting a sequence inside an
+// item (its own merge, its partly filled blocks, the waves it leaves idle)
+// costs about as much time as kSeqStartCost blocks. A sequence shorter than
+// an average item (A = floor(NB / P) blocks) is charged that much more; a
+// longer one starts at or near an item boundary anyway and is not:
+//
+//   s_b   = kSeqStartCost if 0 < nb_b < A, else 0
+//   c_b   = nb_b + s_b (0 for an empty sequence)
+//   coff_b = sum_{b' < b} c_b', C = sum_b c_b
+//   item i covers costs [floor(i C / P), floor((i + 1) C / P)); a cost
+//   position c inside sequence b (coff_b <= c < coff_b + c_b) is block
+//   off_b + max(0, c - coff_b - s_b) (the charge comes first), and C is
+//   block NB. Item i covers the blocks between its two ends, so the items
+//   tile [0, NB) in order. Without short sequences this is the plain block
+//   plan lo_i = floor(i NB / P); with one, C >= NB + kSeqStartCost and
+//   NB > 8 (P - 1) make every item's cost range longer than a charge, so
+//   every item holds at least one block.
 //
 // An item may span several sequences (segments). A sequence lying inside
 // one item is finished there; a longer one leaves one split state per item
@@ -50,16 +65,32 @@ __host__ __device__ inline int32_t seq_blocks(int32_t n) {
   return (n + kBlockTokens - 1) / kBlockTokens;
 }
 
+constexpr int kSeqStartCost = 4;   // plan charge per short sequence, in blocks
+
+// Whether a sequence of `blocks` blocks is charged its start: 0 < blocks <
+// A = floor(NB / P), written without a division as (blocks + 1) P <= NB.
+__host__ __device__ inline bool seq_charged(int32_t blocks, int64_t nb_total, int32_t items) {
+  return blocks > 0 && (int64_t)(blocks + 1) * items <= nb_total;
+}
+
+// The sequence's length in the plan's cost stream.
+__host__ __device__ inline int32_t seq_cost(int32_t blocks, int64_t nb_total, int32_t items) {
+  return blocks + (seq_charged(blocks, nb_total, items) ? kSeqStartCost : 0);
+}
+
 __host__ __device__ inline int32_t items_per_head(int64_t nb_total, int32_t per_head) {
   if (nb_total <= 0) return 0;
   const int64_t p = (nb_total + kMinItemBlocks - 1) / kMinItemBlocks;
   return p < per_head ? (int32_t)p : per_head;
 }
 
-__host__ __device__ inline int64_t item_lo(int64_t i, int64_t nb_total, int64_t items) {
-  return i * nb_total / items;
+// Start of item i in a stream of `total` units (blocks or costs) cut into
+// `items` near-equal ranges.
+__host__ __device__ inline int64_t item_lo(int64_t i, int64_t total, int64_t items) {
+  return i * total / items;
 }
 
+// The item whose range holds unit x (the inverse of item_lo).
 __host__ __device__ inline int32_t item_of_block(int64_t x, int64_t nb_total, int64_t items) {
   return (int32_t)(((x + 1) * items + nb_total - 1) / nb_total - 1);
 }

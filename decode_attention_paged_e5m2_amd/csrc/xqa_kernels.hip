@@ -189,6 +189,15 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// A wave-uniform 64-bit value marked uniform for the compiler (it keeps
+// what it cannot prove uniform, and everything derived from it, in vector
+// registers).
+__device__ __forceinline__ long long uniform64(long long v) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 struct SeqInfo {
   int b;          // sequence index
   int n;          // clamped length
@@ -209,21 +218,27 @@ struct SeqTable {
   bool small;               // batch <= 64
   int n_l;                  // small: clamped length of sequence `lane` (0 past the batch)
   int excl_l;               // small: first block of sequence `lane`
+  int cexcl_l;              // small: first cost unit of sequence `lane` (plan cost stream)
+  int charge_l;             // small: the plan's charge for sequence `lane` (0 or kSeqStartCost)
   int nch;                  // large: 64-sequence chunks
   const long long* off;     // large: [nch + 1] blocks before each chunk (LDS)
+  const long long* coff;    // large: [nch + 1] cost units before each chunk (LDS)
   const int* has_empty;     // large: [nch] nonzero when the chunk holds an empty sequence (LDS)
   long long nb;             // total blocks per head
+  int items;                // P: work items per head
+  long long ctot;           // total cost units per head (nb when no sequence is charged)
   bool any_empty;           // some sequence of the batch has no token
 
   // Called by every thread of the workgroup (the large path synchronises the
-  // workgroup). lds: room for kMaxBatch / 64 + 1 values; lds_empty: for
-  // kMaxBatch / 64 + 1 flags (the last one: any chunk has one).
-  __device__ SeqTable(const int32_t* c, int bt, int mt, int lane, int wave, long long* lds,
-                      int* lds_empty)
-      : ctx(c), batch(bt), max_tokens(mt), small(bt <= 64), n_l(0), excl_l(0), nch(0), off(lds),
-        has_empty(lds_empty), nb(0), any_empty(false) {
+  // workgroup). lds, lds_cost: room for kMaxBatch / 64 + 1 values each;
+  // lds_empty: for kMaxBatch / 64 + 1 flags (the last one: any chunk has one).
+  __device__ SeqTable(const int32_t* c, int bt, int mt, int per_head, int lane, int wave,
+                      long long* lds, long long* lds_cost, int* lds_empty)
+      : ctx(c), batch(bt), max_tokens(mt), small(bt <= 64), n_l(0), excl_l(0), cexcl_l(0),
+        charge_l(0), nch(0), off(lds), coff(lds_cost), has_empty(lds_empty), nb(0), items(0),
+        ctot(0), any_empty(false) {
     if (small) {
-      init_small(lane);
+      init_small(lane, per_head);
       return;
     }
     nch = (batch + 63) >> 6;
@@ -267,6 +282,37 @@ struct SeqTable {
     __syncthreads();
     nb = lds[nch];
     any_empty = lds_empty[nch] != 0;
+    items = items_per_head(nb, per_head);
+    // Second pass: the chunks' costs, now that P is known (the lengths are
+    // cache hits).
+    for (int c0 = 8 * wave; c0 < nch; c0 += 8 * kWaves) {
+      int v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = 64 * (c0 + k) + lane;
+        const int n = clamp_len(ctx[min(i, batch - 1)], max_tokens);
+        v[k] = i < batch ? seq_cost(seq_blocks(n), nb, items) : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const unsigned tot = (unsigned)__builtin_amdgcn_readlane(wave_inclusive_scan(v[k]), 63);
+        if (lane == 0 && c0 + k < nch) lds_cost[c0 + k] = tot;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      long long crun = 0;
+      for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int cc = c0 + lane;
+        const unsigned tc = cc < nch ? (unsigned)lds_cost[cc] : 0u;
+        const unsigned cincl = (unsigned)wave_inclusive_scan((int)tc);
+        if (cc < nch) lds_cost[cc] = crun + cincl - tc;
+        crun += (unsigned)__builtin_amdgcn_readlane((int)cincl, 63);
+      }
+      if (lane == 0) lds_cost[nch] = crun;
+    }
+    __syncthreads();
+    ctot = lds_cost[nch];
   }
 
   // Whether sequence b (this lane's; b < batch when in_batch) has no token.
@@ -282,12 +328,24 @@ struct SeqTable {
     return in_batch && has_empty[b >> 6] && clamp_len(ctx[b], max_tokens) == 0;
   }
 
-  __device__ void init_small(int lane) {
+  __device__ void init_small(int lane, int per_head) {
     n_l = lane < batch ? clamp_len(ctx[lane], max_tokens) : 0;
     const int b_l = seq_blocks(n_l);
     const int incl = wave_inclusive_scan(b_l);   // <= 64 * 2^19: no overflow
     excl_l = incl - b_l;
     nb = __builtin_amdgcn_readlane(incl, 63);
+    items = items_per_head(nb, per_head);
+    const bool charged = seq_charged(b_l, nb, items);
+    if (__ballot(charged) != 0) {
+      charge_l = charged ? kSeqStartCost : 0;
+      const int cost = b_l + charge_l;
+      const int cincl = wave_inclusive_scan(cost);   // <= 64 * (2^19 + 4): no overflow
+      cexcl_l = cincl - cost;
+      ctot = __builtin_amdgcn_readlane(cincl, 63);
+    } else {   // no charge: the cost stream is the block stream
+      cexcl_l = excl_l;
+      ctot = nb;
+    }
     any_empty = __ballot(lane < batch && n_l == 0) != 0;
   }
 
@@ -339,6 +397,47 @@ struct SeqTable {
     const int src = __ffsll((unsigned long long)hit) - 1;
     return {64 * c + src, __builtin_amdgcn_readlane(n, src),
             off[c] + (unsigned)__builtin_amdgcn_readlane(excl, src)};
+  }
+
+  // Cost position c of the plan: the block it stands for (nb for c >= ctot)
+  // and, for c < ctot, the non-empty sequence whose cost range holds it
+  // (that sequence also holds the block).
+  __device__ long long block_at_cost(long long c, int lane, SeqInfo* seq) const {
+    *seq = SeqInfo{batch, 0, nb};
+    if (c >= ctot) return nb;
+    if (small) {
+      const unsigned long long m = __ballot(n_l > 0 && (long long)cexcl_l <= c);
+      if (!m) return nb;   // not reached: the first non-empty sequence starts at cost 0
+      const int src = 63 - __clzll((long long)m);
+      const long long first = (long long)__builtin_amdgcn_readlane(excl_l, src);
+      const long long local = c - (long long)__builtin_amdgcn_readlane(cexcl_l, src) -
+                              __builtin_amdgcn_readlane(charge_l, src);
+      *seq = SeqInfo{src, __builtin_amdgcn_readlane(n_l, src), first};
+      return first + (local > 0 ? local : 0);
+    }
+    // The first chunk whose cost end passes c.
+    int k = nch;
+    for (int g = 0; g < nch; g += 64) {
+      const unsigned long long hit = __ballot(coff[min(g + lane + 1, nch)] > c);
+      if (hit) {
+        k = g + __ffsll((unsigned long long)hit) - 1;
+        break;
+      }
+    }
+    if (k >= nch) return nb;
+    int n, excl, blocks;
+    load_chunk(k, lane, n, excl, blocks);
+    const int cost = seq_cost(blocks, nb, items);
+    const int cexcl = wave_inclusive_scan(cost) - cost;
+    const long long clo = coff[k] + (unsigned)cexcl;
+    const unsigned long long hit = __ballot(blocks > 0 && c >= clo && c < clo + cost);
+    if (!hit) return nb;   // not reached
+    const int src = __ffsll((unsigned long long)hit) - 1;
+    const long long first = off[k] + (unsigned)__builtin_amdgcn_readlane(excl, src);
+    const int charge = __builtin_amdgcn_readlane(cost - blocks, src);
+    const long long local = c - (coff[k] + (unsigned)__builtin_amdgcn_readlane(cexcl, src)) - charge;
+    *seq = SeqInfo{64 * k + src, __builtin_amdgcn_readlane(n, src), first};
+    return first + (local > 0 ? local : 0);
   }
 };
 
@@ -540,6 +639,7 @@ struct SplitShared {
   float l[kWaves][kMaxGroup];
   float o[kWaves][kMaxGroup][kHeadDim + 4];
   long long chunk_off[kMaxBatch / 64 + 1];   // batches over 64: blocks before each 64-sequence chunk
+  long long chunk_coff[kMaxBatch / 64 + 1];  // batches over 64: plan cost units before each chunk
   int chunk_empty[kMaxBatch / 64 + 1];       // batches over 64: the chunk holds an empty sequence;
                                              // last used entry: any chunk does
 };
@@ -722,9 +822,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
   const int wave = threadIdx.x >> 6;
   const int Hkv = a.num_kv_heads;
 
-  const SeqTable seqs(context_lens, batch, max_tokens, lane, wave, sh.chunk_off, sh.chunk_empty);
-  const long long NB = seqs.nb;
-  const int P = items_per_head(NB, a.per_head);
+  const SeqTable seqs(context_lens, batch, max_tokens, a.per_head, lane, wave, sh.chunk_off,
+                      sh.chunk_coff, sh.chunk_empty);
+  const int P = seqs.items;
   const int item = blockIdx.x / Hkv;
   const int h = blockIdx.x % Hkv;
   // Empty sequences: zero rows and a merge record with no states, written
@@ -756,8 +856,31 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
     finish_empty();
     return;
   }
-  const long long lo = item_lo(item, NB, P);
-  const long long hi = item_lo(item + 1, NB, P);
+  // The item's block range, from its two ends in the plan's cost stream (the
+  // block stream itself when no sequence is charged); the sequence holding
+  // its first block comes with it.
+  long long lo, hi;
+  SeqInfo sq;
+  if (seqs.ctot == seqs.nb) {
+    lo = item_lo(item, seqs.nb, P);
+    hi = item_lo(item + 1, seqs.nb, P);
+    sq = seqs.containing(lo, lane);
+  } else {
+    SeqInfo sq_end;
+    lo = seqs.block_at_cost(item_lo(item, seqs.ctot, P), lane, &sq);
+    hi = seqs.block_at_cost(item_lo(item + 1, seqs.ctot, P), lane, &sq_end);
+  }
+  // The same on every lane; marked so for the compiler, which does not see
+  // it through the lookups.
+  lo = uniform64(lo);
+  hi = uniform64(hi);
+  sq.b = __builtin_amdgcn_readfirstlane(sq.b);
+  sq.n = __builtin_amdgcn_readfirstlane(sq.n);
+  sq.off = uniform64(sq.off);
+  if (lo >= hi || sq.b >= batch) {   // not reached: every item holds a block
+    finish_empty();
+    return;
+  }
 
   const int g = lane & 15;
   const int q = lane >> 4;
@@ -798,7 +921,6 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
     return s;
   };
 
-  SeqInfo sq = seqs.containing(lo, lane);
   Segment cur = make_segment(sq, true);
   WaveSeg cw = wave_seg(a, cur, lane, wave);
   half8 qf[4];

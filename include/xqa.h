@@ -281,8 +281,10 @@ xqa_status_t xqa_decode_pages(xqa_handle_t handle, const void* q, const uint8_t*
 /* Host mirror of the device-side plan, for diagnostics and tests:
  * context_lens_host is host memory [batch]. Each KV head's token stream
  * (sequences in batch order, each rounded up to 32-token blocks) is cut into
- * equal block ranges, one per work item. Writes the largest work item in
- * tokens and the number of work items (all heads) the device would use. */
+ * contiguous block ranges, one per work item, of near-equal cost, where a
+ * non-empty sequence costs its blocks plus 4 (the price of starting it
+ * inside an item). Writes the largest work item in tokens and the number of
+ * work items (all heads) the device would use. */
 xqa_status_t xqa_plan(xqa_handle_t handle, const int32_t* context_lens_host, int32_t batch,
                       int32_t* split_tokens, int32_t* num_items);
 

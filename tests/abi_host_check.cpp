@@ -239,8 +239,11 @@ int main() {
   int32_t split = 0, items = 0;
   EXPECT(xqa_plan(h, host_lens, 3, &split, &items) == XQA_OK);
   const long long nb = 4 + 0 + 157;   // ceil(100/32) + ceil(5000/32)
-  const int P = xqa::items_per_head(nb, 128);
-  EXPECT(items == P * 4 && split == (int)((nb + P - 1) / P) * 32);
+  const int P = xqa::items_per_head(nb, 128);   // 21
+  // A = 161 / 21 = 7: the 4-block sequence is charged (cost 8), the other
+  // is not (157): C = 165, item ends floor(i * 165 / 21) map to blocks 0, 3,
+  // 11, 19, ..., 153, 161; the largest items hold 8 blocks.
+  EXPECT(items == P * 4 && split == 8 * 32);
   EXPECT(xqa_destroy(h) == XQA_OK);
 
   // A handle whose bounds never split a sequence: one kernel per step, and

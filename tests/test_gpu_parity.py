@@ -123,24 +123,37 @@ def test_work_item_boundaries():
 
 def _states_of(ctx, b, per_head):
     # Split states sequence b leaves, from the plan's published formulas:
-    # 32-token blocks, P = min(per_head, ceil(NB / 8)) items of equal size.
+    # 32-token blocks, P = min(per_head, ceil(NB / 8)) items cut at equal
+    # cost, a sequence shorter than NB // P blocks costing its blocks plus 4;
+    # the number of items whose block range meets sequence b's blocks.
     nb = [-(-max(int(n), 0) // 32) for n in ctx]
     NB = sum(nb)
     P = min(per_head, -(-NB // 8))
-    off = sum(nb[:b])
-    item = lambda x: ((x + 1) * P + NB - 1) // NB - 1
-    return item(off + nb[b] - 1) - item(off) + 1
+    charge = [4 if 0 < x < NB // P else 0 for x in nb]
+    cost = [x + c if x > 0 else 0 for x, c in zip(nb, charge)]
+    C = sum(cost)
+    off = [sum(nb[:i]) for i in range(len(nb))]
+    coff = [sum(cost[:i]) for i in range(len(nb))]
+
+    def block_at(c):
+        if c >= C:
+            return NB
+        i = max(j for j in range(len(nb)) if cost[j] > 0 and coff[j] <= c)
+        return off[i] + max(0, c - coff[i] - charge[i])
+
+    ends = [block_at(i * C // P) for i in range(P + 1)]
+    return sum(1 for i in range(P) if ends[i] < off[b] + nb[b] and ends[i + 1] > off[b])
 
 
 @pytest.mark.parametrize("hkv,hq", [(1, 8), (1, 16), (2, 6)])
 def test_combine_state_counts(hkv, hq):
-    # One long sequence between two short ones, split over 15 to 129 work
+    # One long sequence between two short ones, split over 14 to 148 work
     # items: a single round of split states, then several rounds shared out
     # over the combine's waves (some waves with none), with 8, 16 and 3 query
     # rows per KV head.
     rng = np.random.default_rng(77 + hq)
     seen = []
-    for per_head in (15, 16, 17, 18, 33, 34, 66, 100, 130):
+    for per_head in (15, 16, 17, 18, 19, 33, 34, 66, 100, 150):
         n = per_head * 8 * 32 + int(rng.integers(0, 256))
         ctx = [300, n, 50]
         pages = -(-n // 16)
