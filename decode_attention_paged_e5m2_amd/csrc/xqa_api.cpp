@@ -27,14 +27,14 @@ struct Geometry {
   int combine_waves;    // waves per combine workgroup
   bool direct_only;     // no sequence can leave split states: one kernel per step
   size_t partial_bytes; // 2 * grid records
-  size_t desc_bytes;    // merge descriptors: max_batch * Hkv int2, after the records
+  size_t desc_bytes;    // merge records: max_batch * Hkv int2, after the split states
 };
 
 struct xqa_handle_s {
   xqa_config_t cfg;
   int device;
   Geometry geo;
-  float* partials;    // workspace: 2 * grid split-state records, then the merge descriptors
+  float* partials;    // workspace: 2 * grid split-state records, then the merge records
   int32_t* vtable;    // page-subset decode: [max_batch][max_selected_pages] page ids, then
   int32_t* vlens;     //   [max_batch] lengths (null when max_selected_pages is 0)
   size_t workspace_bytes;

@@ -5,17 +5,19 @@
 // sequence attends over its paged E5M2 K/V cache, query heads sharing KV
 // heads. The same kernels also take several new query tokens per sequence
 // (causal among themselves), an E4M3 cache with per-tensor K/V scales, and
-// a small kernel writes each step's new token into the cache. The phases that page lists -- K load + E5M2 conversion, QK, V load
-// + conversion, PV, synchronisation -- map onto the code below; the tiling
-// is designed for CDNA4 (64-wide waves, MFMA, DPP) rather than taken from it.
+// a small kernel writes each step's new token into the cache. The phases
+// that page lists -- K load + E5M2 conversion, QK, V load + conversion, PV,
+// synchronisation -- map onto the code below; the tiling is designed for
+// CDNA4 (64-wide waves, MFMA, DPP) rather than taken from it.
 //
 // A decode step is two kernels. In the split kernel each workgroup is one
 // work item = (sequence, KV head, token range); its four waves take
 // interleaved 32-token blocks (2 pages):
 //
-//   Plan: every workgroup derives the split length and its own item from
-//      context_lens (O(batch) integer work), so the grid is fixed and a
-//      captured graph replays exactly with new lengths.
+//   Plan: every workgroup derives its own item from context_lens (O(batch)
+//      integer work; items are cut evenly by cost, a sequence shorter than
+//      an average item being charged for its start), so the grid is fixed
+//      and a captured graph replays exactly with new lengths.
 //   Gather: a wave fetches the page ids of its next 32 blocks with one
 //      vector load and reads them out with v_readlane; K and V of a block are
 //      eight 16-byte loads per lane, issued one block ahead (ping-pong). The
@@ -30,9 +32,10 @@
 //      instruction for E4M3 (every E4M3 value is a binary16 value).
 //   QK: S^T = K . Q^T with v_mfma_f32_16x16x32_f16, M = the 16 tokens of a
 //      page, N = the query rows (the G heads of the group times the M query
-//      tokens, padded to 16), four MFMAs over head_dim 128. The contraction index may be permuted freely as
-//      long as the K and Q fragments agree, which is what lets K go straight
-//      from its load layout into the A operand.
+//      tokens, padded to 16), four MFMAs over head_dim 128. The contraction
+//      index may be permuted freely as long as the K and Q fragments agree,
+//      which is what lets K go straight from its load layout into the A
+//      operand.
 //   Softmax: the accumulator gives lane l the scores of query row l%16 for
 //      tokens 4q..4q+3; the block max over a 32-token block is a register
 //      max plus two lane-swap steps (16, 32). Scores are kept in base-2
@@ -50,16 +53,17 @@
 //      all-ones A operand.
 //   Merge: the four waves' (max, sum, O) states merge in LDS. A sequence
 //      that fits one item is normalised and written directly; otherwise the
-//      item stores its state in the workspace.
+//      item stores its state in the workspace, and the segments at the
+//      sequence's two ends write its merge record (where its states are).
+//      Empty sequences get zero rows, spread over the grid.
 //
-// The combine kernel then merges the states of every split sequence with
-// the exact log-sum-exp rule M = max m_s, L = sum l_s 2^(m_s-M),
-// out = v_scale * sum 2^(m_s-M) O_s / L (in rounds of loaded states; a long
-// sequence's rounds are shared out over the workgroup's four waves,
-// whose partial merges then meet in LDS in a fixed order), and writes the
-// zero rows of empty sequences. On a handle whose bounds never split a
-// sequence, the split kernel writes those zero rows itself and the step is
-// that one kernel.
+// The combine kernel then merges the states of every split sequence, found
+// through its merge record, with the exact log-sum-exp rule M = max m_s,
+// L = sum l_s 2^(m_s-M), out = v_scale * sum 2^(m_s-M) O_s / L (in rounds of
+// loaded states; a long sequence's rounds are shared out over the
+// workgroup's four waves, whose partial merges then meet in LDS in a fixed
+// order). On a handle whose bounds never split a sequence the step is the
+// split kernel alone.
 // The kernel boundary makes the split states visible across the chip's
 // separately cached dies without any in-kernel cache write-back.
 //
@@ -208,10 +212,12 @@ struct SeqInfo {
 // leaves sequence `lane`'s length and block prefix in lane registers, and
 // every later lookup is a v_readlane or a ballot with no memory access.
 // Larger batches keep, per 64-sequence chunk c, the number of blocks before
-// it (off[c], off[nch] = total), built once per workgroup in LDS (the four
-// waves share out the chunks, eight chunk loads in flight per wave). A lookup
-// is then one load of a chunk's lengths and a scan; finding the chunk that
-// holds a block is a ballot over the table, 64 chunks per step.
+// it (off[c], off[nch] = total) and the plan's cost units before it
+// (coff[c]), built once per workgroup in LDS (the four waves share out the
+// chunks, eight chunk loads in flight per wave; the costs in a second pass,
+// once the item count is known). A lookup is then one load of a chunk's
+// lengths and a scan; finding the chunk that holds a block or a cost
+// position is a ballot over the table, 64 chunks per step.
 struct SeqTable {
   const int32_t* ctx;
   int batch, max_tokens;
@@ -732,7 +738,7 @@ __device__ __forceinline__ void append_if_owner(const AttendArgs& a, const Segme
 
 // The four waves' states of a segment meet in LDS (fixed order); the merged
 // (max, sum, O) is normalised and written, or stored as a split state.
-// The segments at a sequence's ends also fill in its merge descriptor
+// The segments at a sequence's ends also fill in its merge record
 // {slot of the first state, item of the last}: the first segment writes the
 // slot, the last one its item; a sequence inside one item writes {-1, -1}.
 __device__ __forceinline__ void finish_segment(const AttendArgs& a, SplitShared& sh,
@@ -1006,7 +1012,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
 
 // ----------------------------------------------------------- combine kernel
 // The combine kernel needs neither the lengths nor the plan: it reads the
-// merge descriptor the split kernel wrote for its (sequence, KV head).
+// merge record the split kernel wrote for its (sequence, KV head).
 // Workgroups of W waves (W = 1, or 4 when a sequence can leave more states
 // than one round holds) merge each sequence's split states with the
 // log-sum-exp rule, reading states in rounds of kCombineRound with every load
