@@ -189,6 +189,34 @@ def test_large_batches(batch, per_head):
     log(f"large batch={batch} per_head={per_head} S={S} items={items}", st)
 
 
+def test_random_batches_mixing_short_long_and_empty():
+    # Seeded random batches on both sides of 64 sequences, random head
+    # shapes and few work items per head: items full of short sequences
+    # (charged their start by the plan), long sequences split over many
+    # items, empty ones; every output row against the oracle.
+    rng = np.random.default_rng(4242)
+    for case in range(12):
+        batch = int(rng.choice([3, 17, 40, 64, 65, 90]))
+        hkv, g = [(1, 8), (2, 4), (4, 8), (2, 1), (1, 16), (3, 2)][case % 6]
+        per_head = int(rng.choice([1, 2, 5, 13, 0]))
+        kind = rng.random(batch)
+        ctx = np.where(kind < 0.5, rng.integers(1, 70, batch),
+                       np.where(kind < 0.85, rng.integers(70, 700, batch),
+                                rng.integers(700, 3000, batch)))
+        ctx[rng.random(batch) < 0.1] = 0
+        w = make_custom(ctx.tolist(), hkv, hkv * g, [4243, case])
+        xqa = Xqa(max_batch=batch, num_q_heads=hkv * g, num_kv_heads=hkv,
+                  max_pages_per_seq=w.max_pages_per_seq, max_work_items=hkv * per_head)
+        out, _, _ = run(w, xqa=xqa)
+        S, items = xqa.plan(w.context_lens)
+        st = assert_parity(out, reference(w), f"random case {case} batch={batch} hkv={hkv} "
+                                              f"g={g} per_head={per_head}")
+        assert (out[ctx == 0] == 0).all()
+        log(f"random case {case} batch={batch} hkv={hkv} g={g} per_head={per_head} "
+            f"S={S} items={items}", st)
+        xqa.close()
+
+
 def test_zero_and_negative_lengths_and_clamp():
     # Sequence 3 fills its three pages; a length beyond the block table's
     # capacity clamps to 3 * 16 = 48 tokens.
