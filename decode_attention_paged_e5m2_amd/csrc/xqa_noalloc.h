@@ -5,7 +5,8 @@
 
 namespace xqa {
 
-// Size of the fixed workspace on each device: split-state records.
+// Size of the fixed workspace on each device: split-state records, then the
+// per-(sequence, KV head) merge records.
 constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
 
 struct NoallocDevice {

@@ -12,8 +12,8 @@
 namespace xqa {
 namespace {
 
-// Split-state records of one decode call at a time (each call writes every
-// record it reads, so no contents carry over between calls).
+// Split-state and merge records of one decode call at a time (each call
+// writes every record it reads, so no contents carry over between calls).
 static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 constexpr int kMaxDevices = 64;
