@@ -17,12 +17,13 @@ ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for all device code. MFMA results
 # are kept in ordinary VGPRs (no AGPR copies around the softmax arithmetic).
-# The first four dwords of kernel arguments are preloaded into SGPRs at wave
-# launch (the attention kernels put the plan's inputs there).
+# Up to 16 leading scalar argument dwords are preloaded into SGPRs at wave
+# launch (the split kernel puts the plan's inputs there, the combine kernel
+# every value it reads), so they need no load from the argument block.
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=4",
+    "-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", INCLUDE,
 ]
 

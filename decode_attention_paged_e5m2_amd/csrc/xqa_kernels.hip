@@ -1030,6 +1030,15 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const int32_t* context_
 // on the state count only, so the result is the same on every run. Rounds
 // of 8 rather than 16 here keep the kernel at ~100 VGPRs instead of ~155,
 // which measured faster for both paths.
+//
+// The kernel's path is short, so its set-up counts:
+// - Every value it reads besides the records and states comes as a leading
+//   scalar argument. All 13 dwords are preloaded into SGPRs, so nothing
+//   waits for the argument block, which arrives ~1 us after launch.
+// - State addresses come from one running pointer, since states after the
+//   first are a fixed stride apart, not from a 64-bit product per state.
+//   The scalar unit a CU's waves share spent ~0.3 us more on those
+//   products than the states take to arrive.
 
 // Merges one round of split states (cnt valid entries) into (M, L, o[0..N)).
 // A state of a query row that saw no token has m = -inf and weight 0; equal
@@ -1063,14 +1072,21 @@ struct CombineShared {
 
 template <int W>
 __global__ __launch_bounds__(64 * W) void combine_kernel(const int2* merge_desc, int32_t hkv,
-                                                         int32_t per_head, AttendArgs a) {
+                                                         int32_t per_head, const float* partials,
+                                                         int32_t item_stride, int32_t rows,
+                                                         uint16_t* out, int32_t group,
+                                                         int32_t q_tokens, float v_scale) {
   constexpr int kWgCols = 16 * W;
   constexpr int kChunks = kHeadDim / kWgCols;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int R = a.rows;
+  const int R = rows;
   const int Hkv = hkv;
   const int chunk = blockIdx.x % kChunks;
+  auto orow = [&](int bb, int hh, int r) {
+    return out + (((long long)bb * q_tokens + r / group) * Hkv * group + (long long)hh * group +
+                  r % group) * kHeadDim;
+  };
   const int bh = blockIdx.x / kChunks;
   const int b = bh / Hkv;
   const int h = bh % Hkv;
@@ -1089,12 +1105,12 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int2* merge_desc,
   if (slot0 < 0 || desc.y <= i0 || desc.y >= per_head) return;
   const int nsb = desc.y - i0 + 1;
   const int mo = R * kHeadDim;
-  auto rec = [&](int s) {
-    const int slot = s == 0 ? slot0 : 2 * (i0 + s);
-    return a.partials + ((long long)slot * Hkv + h) * a.item_stride;
-  };
+  // State s > 0 sits in slot 2 (i0 + s): consecutive states are `step` floats apart.
+  const long long step = 2LL * Hkv * item_stride;
+  const float* first = partials + ((long long)slot0 * Hkv + h) * item_stride;
+  const float* second = partials + ((long long)(2 * (i0 + 1)) * Hkv + h) * item_stride;
 
-  if (W == 1 || nsb <= kCombineRound) {
+  if (__builtin_expect(W == 1 || nsb <= kCombineRound, 1)) {
     // With W = 1 the handle bounds the state count by kCombineRound, so
     // every instantiation merges a single round here.
     for (int e = lane; e < R * 8; e += 64) {
@@ -1103,9 +1119,13 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int2* merge_desc,
       float mv[kCombineRound], lv[kCombineRound], ov[kCombineRound][2];
       // Unconditional loads (slots past the last state re-read it and are
       // masked in the merge), so the whole round is in flight at once.
+      const float* rk = second;
+      const float* last = first;
 #pragma unroll
       for (int k = 0; k < kCombineRound; ++k) {
-        const float* r = rec(min(k, nsb - 1));
+        if (k > 0 && k < nsb) last = rk;
+        if (k > 0) rk += step;
+        const float* r = k == 0 ? first : last;
         const float2 v = *(const float2*)(r + gg * kHeadDim + c);
         ov[k][0] = v.x;
         ov[k][1] = v.y;
@@ -1114,8 +1134,8 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int2* merge_desc,
       }
       float M = -INFINITY, L = 0.f, o[2] = {0.f, 0.f};
       merge_round<kCombineRound, 2>(mv, lv, ov, min(nsb, kCombineRound), M, L, o);
-      const float inv = L > 0.f ? a.v_scale / L : 0.f;   // a row with no visible token is zero
-      *(uint32_t*)(out_row(a, b, h, gg) + c) = pack_half2(o[0] * inv, o[1] * inv);
+      const float inv = L > 0.f ? v_scale / L : 0.f;   // a row with no visible token is zero
+      *(uint32_t*)(orow(b, h, gg) + c) = pack_half2(o[0] * inv, o[1] * inv);
     }
     return;
   }
@@ -1129,11 +1149,14 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int2* merge_desc,
       const int c = chunk * kWgCols + (e & 7) * 8;
       float M = -INFINITY, L = 0.f;
       float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const float* lastp = second + (long long)(nsb - 2) * step;   // nsb > 16 here
       for (int s0 = kCombineSharedRound * wave; s0 < nsb; s0 += kCombineSharedRound * W) {
         float mv[kCombineSharedRound], lv[kCombineSharedRound], ov[kCombineSharedRound][8];
+        const float* rk = second + (long long)(s0 > 0 ? s0 - 1 : 0) * step;   // state max(s0, 1)
 #pragma unroll
         for (int k = 0; k < kCombineSharedRound; ++k) {
-          const float* r = rec(min(s0 + k, nsb - 1));
+          const float* r = s0 + k == 0 ? first : (s0 + k < nsb ? rk : lastp);
+          if (s0 + k > 0) rk += step;
           const float4v v0 = *(const float4v*)(r + gg * kHeadDim + c);
           const float4v v1 = *(const float4v*)(r + gg * kHeadDim + c + 4);
 #pragma unroll
@@ -1167,13 +1190,13 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int2* merge_desc,
         o0 += f * sh.o[w][e][0];
         o1 += f * sh.o[w][e][1];
       }
-      const float inv = L > 0.f ? a.v_scale / L : 0.f;
+      const float inv = L > 0.f ? v_scale / L : 0.f;
       uint4 packed;
       packed.x = pack_half2(o0[0] * inv, o0[1] * inv);
       packed.y = pack_half2(o0[2] * inv, o0[3] * inv);
       packed.z = pack_half2(o1[0] * inv, o1[1] * inv);
       packed.w = pack_half2(o1[2] * inv, o1[3] * inv);
-      *(uint4*)(out_row(a, b, h, e >> 3) + chunk * kWgCols + (e & 7) * 8) = packed;
+      *(uint4*)(orow(b, h, e >> 3) + chunk * kWgCols + (e & 7) * 8) = packed;
     }
   }
 }
@@ -1252,11 +1275,13 @@ hipError_t launch_combine(const AttendArgs& a, hipStream_t stream) {
     constexpr int W = kCombineMaxWaves;
     const int grid = a.batch * a.num_kv_heads * (kHeadDim / (16 * W));
     hipLaunchKernelGGL(combine_kernel<W>, dim3(grid), dim3(64 * W), 0, stream, a.merge_desc,
-                       a.num_kv_heads, a.per_head, a);
+                       a.num_kv_heads, a.per_head, a.partials, a.item_stride, a.rows, a.out,
+                       a.group, a.q_tokens, a.v_scale);
   } else {
     const int grid = a.batch * a.num_kv_heads * (kHeadDim / 16);
     hipLaunchKernelGGL(combine_kernel<1>, dim3(grid), dim3(64), 0, stream, a.merge_desc,
-                       a.num_kv_heads, a.per_head, a);
+                       a.num_kv_heads, a.per_head, a.partials, a.item_stride, a.rows, a.out,
+                       a.group, a.q_tokens, a.v_scale);
   }
   return hipGetLastError();
 }
