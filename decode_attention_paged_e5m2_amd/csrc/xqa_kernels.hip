@@ -1205,21 +1205,29 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int2* merge_desc,
 // One thread per (sequence, KV head, K or V, 8 head-dim values): a 16-byte
 // read of the new row, an 8-byte write into the page slot. 16 consecutive
 // threads cover one 128-value row, so reads and writes are contiguous.
-__global__ void append_kernel(AppendArgs a) {
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)a.batch * a.num_kv_heads * 32;
-  if (gid >= total) return;
+constexpr int kAppendThreads = 256;
+
+// The launch grid holds batch * Hkv * 32 < 2^31 threads, so 32-bit indices
+// suffice. All but v_pages arrive preloaded in SGPRs; v_pages, the length
+// and the new row are loaded together.
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(
+    const int32_t* context_lens, const int32_t* block_table, const uint16_t* k_new,
+    const uint16_t* v_new, uint8_t* k_pages, int32_t batch, int32_t num_kv_heads,
+    int32_t max_pages, uint8_t* v_pages) {
+  const unsigned gid = blockIdx.x * kAppendThreads + threadIdx.x;
+  if (gid >= (unsigned)batch * num_kv_heads * 32u) return;
   const int j = (int)(gid & 15);
   const int is_v = (int)((gid >> 4) & 1);
-  const long long bh = gid >> 5;   // b * Hkv + h
-  const int h = (int)(bh % a.num_kv_heads);
-  const int b = (int)(bh / a.num_kv_heads);
-  const int n = a.context_lens[b];
-  if (n <= 0 || n > a.max_tokens) return;   // no slot for this sequence
-  const int t = n - 1;
-  const int page = a.block_table[(long long)b * a.max_pages + t / kPageSize];
-  const uint16_t* src = (is_v ? a.v_new : a.k_new) + bh * kHeadDim + 8 * j;
+  const unsigned bh = gid >> 5;   // b * Hkv + h
+  const int h = (int)(bh % (unsigned)num_kv_heads);
+  const int b = (int)(bh / (unsigned)num_kv_heads);
+  const int n = context_lens[b];
+  const uint16_t* src = (is_v ? v_new : k_new) + (size_t)bh * kHeadDim + 8 * j;
   const u32x4 x = *(const u32x4*)src;
+  asm volatile("" ::"v"(n), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "s"(v_pages));
+  if (n <= 0 || n > max_pages * kPageSize) return;   // no slot for this sequence
+  const int t = n - 1;
+  const int page = block_table[(long long)b * max_pages + t / kPageSize];
   uint32_t packed[2];
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
@@ -1227,8 +1235,8 @@ __global__ void append_kernel(AppendArgs a) {
     packed[w] = e5m2_from_f16(p0 & 0xFFFFu) | (e5m2_from_f16(p0 >> 16) << 8) |
                 (e5m2_from_f16(p1 & 0xFFFFu) << 16) | (e5m2_from_f16(p1 >> 16) << 24);
   }
-  uint8_t* dst = (is_v ? a.v_pages : a.k_pages) +
-                 (((size_t)page * a.num_kv_heads + h) * kPageSize + t % kPageSize) * kHeadDim + 8 * j;
+  uint8_t* dst = (is_v ? v_pages : k_pages) +
+                 (((size_t)page * num_kv_heads + h) * kPageSize + t % kPageSize) * kHeadDim + 8 * j;
   *(uint2*)dst = make_uint2(packed[0], packed[1]);
 }
 
@@ -1288,9 +1296,10 @@ hipError_t launch_combine(const AttendArgs& a, hipStream_t stream) {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const long long total = (long long)a.batch * a.num_kv_heads * 32;
-  const int threads = 256;
-  const long long blocks = (total + threads - 1) / threads;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, a);
+  const long long blocks = (total + kAppendThreads - 1) / kAppendThreads;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(kAppendThreads), 0, stream,
+                     a.context_lens, a.block_table, a.k_new, a.v_new, a.k_pages, a.batch,
+                     a.num_kv_heads, a.max_pages, a.v_pages);
   return hipGetLastError();
 }
 

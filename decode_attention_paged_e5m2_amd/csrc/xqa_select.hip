@@ -36,20 +36,27 @@ __device__ __forceinline__ int wave_inclusive_max0(int v) {
   return v;
 }
 
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(
+    const int32_t* context_lens, const int32_t* select_counts, const int32_t* page_select,
+    const int32_t* block_table, int32_t* vtable, int32_t max_tokens, int32_t select_stride,
+    int32_t max_pages, int32_t vstride, int32_t* vlens) {
   __shared__ int s_max[kSelectWaves];
   __shared__ int s_cnt[kSelectWaves];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n = clamp_len(a.context_lens[b], a.max_tokens);
+  // The length and the count (and vlens, the one argument not preloaded)
+  // are loaded together.
+  const int n_in = context_lens[b];
+  int count = select_counts[b];
+  asm volatile("" ::"s"(n_in), "s"(count), "s"(vlens));
+  const int n = clamp_len(n_in, max_tokens);
   const int used = (n + kPageSize - 1) / kPageSize;
-  int count = a.select_counts[b];
-  count = count < 0 ? 0 : (count > a.select_stride ? a.select_stride : count);
-  const int32_t* sel = a.page_select + (long long)b * a.select_stride;
-  const int32_t* bt = a.block_table + (long long)b * a.max_pages;
-  int32_t* vt = a.vtable + (long long)b * a.vstride;
+  count = count < 0 ? 0 : (count > select_stride ? select_stride : count);
+  const int32_t* sel = page_select + (long long)b * select_stride;
+  const int32_t* bt = block_table + (long long)b * max_pages;
+  int32_t* vt = vtable + (long long)b * vstride;
   int best1 = 0;   // 1 + the largest page kept so far (0: none yet)
   int kept = 0;
   for (int j0 = 0; j0 < count; j0 += kSelectThreads) {
@@ -82,14 +89,16 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     __syncthreads();   // s_max and s_cnt are rewritten by the next tile
   }
   if (tid == 0) {
-    a.vlens[b] = kept == 0 ? 0 : kPageSize * (kept - 1) + min(kPageSize, n - kPageSize * (best1 - 1));
+    vlens[b] = kept == 0 ? 0 : kPageSize * (kept - 1) + min(kPageSize, n - kPageSize * (best1 - 1));
   }
 }
 
 }  // namespace
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(select_kernel, dim3(a.batch), dim3(kSelectThreads), 0, stream, a);
+  hipLaunchKernelGGL(select_kernel, dim3(a.batch), dim3(kSelectThreads), 0, stream,
+                     a.context_lens, a.select_counts, a.page_select, a.block_table, a.vtable,
+                     a.max_tokens, a.select_stride, a.max_pages, a.vstride, a.vlens);
   return hipGetLastError();
 }
 
