@@ -1207,18 +1207,20 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(const int2* merge_desc,
 // threads cover one 128-value row, so reads and writes are contiguous.
 constexpr int kAppendThreads = 256;
 
-// The launch grid holds batch * Hkv * 32 < 2^31 threads, so 32-bit indices
-// suffice. All but v_pages arrive preloaded in SGPRs; v_pages, the length
-// and the new row are loaded together.
+// The grid holds batch * Hkv * 32 threads, which can pass 2^32, so the
+// thread index is 64-bit; b * Hkv + h stays below 2^28 (creation bounds
+// max_batch * Hkv * 8 below 2^31), so the division by Hkv is 32-bit. All
+// arguments but v_pages arrive preloaded in SGPRs; v_pages, the length and
+// the new row are loaded together.
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     const int32_t* context_lens, const int32_t* block_table, const uint16_t* k_new,
     const uint16_t* v_new, uint8_t* k_pages, int32_t batch, int32_t num_kv_heads,
     int32_t max_pages, uint8_t* v_pages) {
-  const unsigned gid = blockIdx.x * kAppendThreads + threadIdx.x;
-  if (gid >= (unsigned)batch * num_kv_heads * 32u) return;
+  const unsigned long long gid = (unsigned long long)blockIdx.x * kAppendThreads + threadIdx.x;
+  if (gid >= (unsigned long long)batch * num_kv_heads * 32u) return;
   const int j = (int)(gid & 15);
   const int is_v = (int)((gid >> 4) & 1);
-  const unsigned bh = gid >> 5;   // b * Hkv + h
+  const unsigned bh = (unsigned)(gid >> 5);   // b * Hkv + h
   const int h = (int)(bh % (unsigned)num_kv_heads);
   const int b = (int)(bh / (unsigned)num_kv_heads);
   const int n = context_lens[b];
