@@ -1,0 +1,105 @@
+"""GPU parity on seeded random mixtures of every input dimension at once:
+batch sizes on both sides of 64, ten head shapes (G = 1 to 16), 1 to 8 query
+tokens per sequence, E5M2 and E4M3 caches with and without per-tensor scales,
+block-table capacities from 128 to 4160 tokens, forced work-item counts,
+zero, negative and clamped lengths, and page subsets with messy selection
+rows. Every output row is compared against the oracle (the page "[Kernel]
+[SM70] Pipeline batched E5M2 XQA decode", sections Purpose and Pending work
+and gates: randomized pages, ragged and boundary lengths)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests._helpers import assert_parity, ensure_library
+from workloads import make_custom
+from workloads.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 1), (1, 8), (2, 4), (4, 8), (8, 2), (3, 5), (1, 16), (2, 16), (6, 1), (4, 3)]
+
+
+def _selection(rng, lens, cap, cap_pages, batch):
+    """Sorted random page subsets of each sequence's used pages, some rows with
+    an out-of-order or out-of-range entry inserted, some counts out of range."""
+    S = cap_pages
+    sel = np.full((batch, S), -1, dtype=np.int32)
+    cnt = np.zeros(batch, dtype=np.int32)
+    for b in range(batch):
+        used = (max(0, min(int(lens[b]), cap)) + 15) // 16
+        k = int(rng.integers(0, S + 1))
+        if used > 0:
+            row = list(np.sort(rng.choice(used, size=min(k, used), replace=False)))
+        else:
+            row = []
+        if rng.random() < 0.3 and len(row) < S:
+            row.insert(int(rng.integers(0, len(row) + 1)), int(rng.integers(-3, used + 5)))
+        row = row[:S]
+        sel[b, :len(row)] = row
+        cnt[b] = len(row) if rng.random() < 0.9 else int(rng.integers(-2, S + 3))
+    return sel, cnt
+
+
+def test_random_mixtures_against_the_oracle():
+    ensure_library()
+    from decode_attention_paged_e5m2_amd import Xqa
+    rng = np.random.default_rng(20261203)
+    for case in range(80):
+        batch = int(rng.choice([1, 2, 3, 5, 8, 16, 31, 33, 64, 65, 100, 150]))
+        hkv, g = SHAPES[case % len(SHAPES)]
+        M = int(rng.choice([m for m in (1, 1, 2, 3, 4, 8) if m <= 16 // g]))
+        fmt = "e4m3" if rng.random() < 0.35 else "e5m2"
+        if rng.random() < 0.5:
+            ks, vs = 1.0, 1.0
+        else:
+            ks, vs = float(rng.choice([0.25, 0.5, 2.0])), float(rng.choice([0.5, 1.5, 3.0]))
+        kind = rng.random(batch)
+        cap_pages = int(rng.choice([8, 40, 130, 260]))
+        cap = cap_pages * 16
+        ctx = np.where(kind < 0.4, rng.integers(1, 80, batch),
+                       np.where(kind < 0.85, rng.integers(80, 900, batch),
+                                rng.integers(900, 4200, batch)))
+        ctx = np.minimum(ctx, cap)
+        ctx[rng.random(batch) < 0.08] = 0
+        clamp = rng.random(batch) < 0.06
+        ctx[clamp] = cap                      # every page of the row is used ...
+        w = make_custom(ctx.tolist(), hkv, hkv * g, [777, case], max_pages_per_seq=cap_pages,
+                        kv_format=fmt)
+        lens = ctx.copy()
+        neg = (ctx == 0) & (rng.random(batch) < 0.5)
+        lens[neg] = -int(rng.integers(1, 100))
+        lens[clamp] = cap + rng.integers(1, 5000, int(clamp.sum()))   # ... and the length clamps
+        per_head = int(rng.choice([0, 0, 1, 2, 3, 7, 16, 50]))
+        pages = M == 1 and fmt == "e5m2"
+        dev = to_device(w)
+        dev_lens = torch.from_numpy(lens.astype(np.int32)).to(dev.q.device)
+        q = rng.standard_normal((batch, M, hkv * g, 128)).astype(np.float16)
+        qq = q if M > 1 else q[:, 0]
+        xqa = Xqa(max_batch=batch, num_q_heads=hkv * g, num_kv_heads=hkv,
+                  max_pages_per_seq=cap_pages, max_work_items=hkv * per_head, max_query_tokens=M,
+                  max_selected_pages=cap_pages if pages else 0)
+        tag = (f"case {case} B={batch} hkv={hkv} g={g} M={M} {fmt} k_scale={ks} v_scale={vs} "
+               f"cap={cap} per_head={per_head}")
+        print(tag, flush=True)
+        kp, vp = w.pools()
+        out = xqa.decode(q=torch.from_numpy(qq).cuda(), k_pages=dev.k_pages, v_pages=dev.v_pages,
+                         block_table=dev.block_table, context_lens=dev_lens, scale=w.scale,
+                         kv_format=fmt, k_scale=ks, v_scale=vs)
+        torch.cuda.synchronize()
+        ref = oracle.decode_attention_fp8(qq, kp, vp, w.block_table, lens, w.scale,
+                                          kv_format=fmt, k_scale=ks, v_scale=vs)
+        assert_parity(out.float().cpu().numpy(), ref, tag)
+        if pages:
+            sel, cnt = _selection(rng, lens, cap, cap_pages, batch)
+            outp = xqa.decode_pages(q=torch.from_numpy(qq).cuda(), k_pages=dev.k_pages,
+                                    v_pages=dev.v_pages, block_table=dev.block_table,
+                                    context_lens=dev_lens, page_select=torch.from_numpy(sel).cuda(),
+                                    select_counts=torch.from_numpy(cnt).cuda(), scale=w.scale)
+            torch.cuda.synchronize()
+            refp = oracle.decode_attention_pages(qq, kp, vp, w.block_table, lens, sel, cnt,
+                                                 w.scale)
+            assert_parity(outp.float().cpu().numpy(), refp, tag + " page subsets")
+        xqa.close()
+        del dev
