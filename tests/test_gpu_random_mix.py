@@ -5,7 +5,10 @@ block-table capacities from 128 to 4160 tokens, forced work-item counts,
 zero, negative and clamped lengths, and page subsets with messy selection
 rows. Every output row is compared against the oracle (the page "[Kernel]
 [SM70] Pipeline batched E5M2 XQA decode", sections Purpose and Pending work
-and gates: randomized pages, ragged and boundary lengths)."""
+and gates: randomized pages, ragged and boundary lengths). The same kind of
+mixtures also go through the paths that must agree bit for bit: the fused
+append + decode against append then decode, the no-alloc entry point against
+a handle, and graph replays against eager calls."""
 
 import numpy as np
 import pytest
@@ -103,3 +106,85 @@ def test_random_mixtures_against_the_oracle():
             assert_parity(outp.float().cpu().numpy(), refp, tag + " page subsets")
         xqa.close()
         del dev
+
+
+def test_random_mixtures_bitwise_paths():
+    # The same kind of random mixtures (one query token, E5M2) through the
+    # paths that must agree bit for bit: the fused append + decode against
+    # the append followed by decode (outputs and pools), xqa_decode_noalloc
+    # against a handle, and graph replays against the eager call.
+    import ctypes
+    lib = ensure_library()
+    from decode_attention_paged_e5m2_amd import Xqa
+    from decode_attention_paged_e5m2_amd._lib import XqaConfig
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    rng = np.random.default_rng(5150)
+    for case in range(30):
+        batch = int(rng.choice([1, 2, 5, 16, 33, 64, 65, 100]))
+        hkv, g = SHAPES[case % len(SHAPES)]
+        cap_pages = int(rng.choice([8, 40, 130, 260]))
+        cap = cap_pages * 16
+        kind = rng.random(batch)
+        ctx = np.where(kind < 0.4, rng.integers(1, 80, batch),
+                       np.where(kind < 0.85, rng.integers(80, 900, batch),
+                                rng.integers(900, 4200, batch)))
+        ctx = np.minimum(ctx, cap)
+        ctx[rng.random(batch) < 0.08] = 0
+        clamp = rng.random(batch) < 0.06
+        ctx[clamp] = cap
+        w = make_custom(ctx.tolist(), hkv, hkv * g, [991, case], max_pages_per_seq=cap_pages)
+        lens = ctx.copy()
+        neg = (ctx == 0) & (rng.random(batch) < 0.5)
+        lens[neg] = -int(rng.integers(1, 100))
+        lens[clamp] = cap + rng.integers(1, 5000, int(clamp.sum()))
+        per_head = int(rng.choice([0, 0, 1, 2, 3, 7, 16]))
+        tag = f"case {case} B={batch} hkv={hkv} g={g} cap={cap} per_head={per_head}"
+        print(tag, flush=True)
+        lens_t = torch.from_numpy(lens.astype(np.int32)).cuda()
+        xqa = Xqa(max_batch=batch, num_q_heads=hkv * g, num_kv_heads=hkv,
+                  max_pages_per_seq=cap_pages, max_work_items=hkv * per_head)
+        k_new = torch.from_numpy((rng.standard_normal((batch, hkv, 128)) * 3).astype(np.float16)).cuda()
+        v_new = torch.from_numpy(rng.standard_normal((batch, hkv, 128)).astype(np.float16)).cuda()
+        sep, fused = to_device(w), to_device(w)
+        xqa.append_kv(k_new=k_new, v_new=v_new, block_table=sep.block_table, context_lens=lens_t,
+                      k_pages=sep.k_pages, v_pages=sep.v_pages)
+        out_sep = xqa.decode(q=sep.q, k_pages=sep.k_pages, v_pages=sep.v_pages,
+                             block_table=sep.block_table, context_lens=lens_t, scale=w.scale)
+        out_fused = xqa.decode_append(q=fused.q, k_new=k_new, v_new=v_new, k_pages=fused.k_pages,
+                                      v_pages=fused.v_pages, block_table=fused.block_table,
+                                      context_lens=lens_t, scale=w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out_fused.view(torch.int16), out_sep.view(torch.int16)), tag
+        assert torch.equal(fused.k_pages, sep.k_pages) and torch.equal(fused.v_pages, sep.v_pages), tag
+        kp, vp = w.pools()
+        kr, vr = oracle.append_kv(kp, vp, w.block_table, lens, k_new.cpu().numpy(),
+                                  v_new.cpu().numpy())
+        ref = oracle.decode_attention(w.q, kr, vr, w.block_table, lens, w.scale)
+        assert_parity(out_fused.float().cpu().numpy(), ref, tag + " append")
+        cfg = XqaConfig(batch, hkv * g, hkv, 128, 16, cap_pages, hkv * per_head, 1, 0)
+        out_na = torch.empty_like(out_sep).fill_(float("nan"))
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        rc = lib.xqa_decode_noalloc(ctypes.byref(cfg), p(sep.q), p(sep.k_pages), p(sep.v_pages),
+                                    p(sep.block_table), p(lens_t), batch, ctypes.c_float(w.scale),
+                                    p(out_na), stream)
+        torch.cuda.synchronize()
+        assert rc == 0, tag
+        assert torch.equal(out_na.view(torch.int16), out_sep.view(torch.int16)), tag + " noalloc"
+        out_g = torch.empty_like(out_sep)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            xqa.decode(q=sep.q, k_pages=sep.k_pages, v_pages=sep.v_pages,
+                       block_table=sep.block_table, context_lens=lens_t, scale=w.scale, out=out_g)
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            xqa.decode(q=sep.q, k_pages=sep.k_pages, v_pages=sep.v_pages,
+                       block_table=sep.block_table, context_lens=lens_t, scale=w.scale, out=out_g)
+        for r in range(3):
+            out_g.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out_g.view(torch.int16), out_sep.view(torch.int16)), f"{tag} replay {r}"
+        del graph
+        xqa.close()
