@@ -11,14 +11,16 @@ namespace {
 // matching length, so the split and combine kernels then run unchanged over
 // only those pages. An entry is kept when it names a page the sequence uses
 // and exceeds every entry kept before it, i.e. when it is in range and above
-// the maximum of the in-range entries before it. Per tile of 1024 entries
-// (one per thread, so a row's loads and its block-table gathers are one
-// memory round trip each): a DPP running maximum inside each wave, the wave
-// maxima through LDS, a ballot per wave for the kept entries and their
-// counts through LDS for the compaction. A kept page's tokens sit at
-// 16 j .. 16 j + 15 of the new table (j its rank); only the last kept page
-// can be the sequence's partial last page, so the new length is
-// 16 (kept - 1) plus what that page holds below n.
+// the maximum of the in-range entries before it. Per tile of 1024 entries,
+// one per thread: a DPP running maximum inside each wave, the wave maxima
+// through LDS, a ballot per wave for the kept entries and their counts
+// through LDS for the compaction. A tile's entry loads and its block-table
+// gathers are one memory round trip each; the gather is issued before the
+// scans, and the first tile's entries are loaded with the length and the
+// count, so a row of one tile costs two dependent round trips. A kept page's
+// tokens sit at 16 j .. 16 j + 15 of the new table (j its rank); only the
+// last kept page can be the sequence's partial last page, so the new length
+// is 16 (kept - 1) plus what that page holds below n.
 constexpr int kSelectWaves = 16;
 constexpr int kSelectThreads = 64 * kSelectWaves;
 
@@ -46,23 +48,30 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // The length and the count (and vlens, the one argument not preloaded)
-  // are loaded together.
-  const int n_in = context_lens[b];
-  int count = select_counts[b];
-  asm volatile("" ::"s"(n_in), "s"(count), "s"(vlens));
-  const int n = clamp_len(n_in, max_tokens);
-  const int used = (n + kPageSize - 1) / kPageSize;
-  count = count < 0 ? 0 : (count > select_stride ? select_stride : count);
   const int32_t* sel = page_select + (long long)b * select_stride;
   const int32_t* bt = block_table + (long long)b * max_pages;
   int32_t* vt = vtable + (long long)b * vstride;
+  // The length, the count, the first tile's entries (every entry below
+  // select_stride is readable, so they need not wait for the count) and
+  // vlens, the one argument not preloaded, are loaded together.
+  const int n_in = context_lens[b];
+  int count = select_counts[b];
+  int praw = sel[tid < select_stride ? tid : select_stride - 1];
+  asm volatile("" ::"s"(n_in), "s"(count), "v"(praw), "s"(vlens));
+  const int n = clamp_len(n_in, max_tokens);
+  const int used = (n + kPageSize - 1) / kPageSize;
+  count = count < 0 ? 0 : (count > select_stride ? select_stride : count);
   int best1 = 0;   // 1 + the largest page kept so far (0: none yet)
   int kept = 0;
   for (int j0 = 0; j0 < count; j0 += kSelectThreads) {
     const int j = j0 + tid;
-    const int p = j < count ? sel[j] : -1;
+    if (j0 > 0) praw = sel[j < count ? j : count - 1];
+    const int p = j < count ? praw : -1;
     const bool in = p >= 0 && p < used;
+    // The physical id of every in-range entry is gathered before the keep
+    // rule is known (p < used <= max_pages; others read entry 0 of the row),
+    // so the gather is in flight during the scans below.
+    const int pid = bt[in ? p : 0];
     const int run = wave_inclusive_max0(in ? p + 1 : 0);
     if (lane == 63) s_max[wave] = run;
     __syncthreads();
@@ -83,7 +92,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
       off += w < wave ? c : 0;
       tile_max = max(tile_max, s_max[w]);
     }
-    if (keep) vt[off + __popcll(mask & ((1ull << lane) - 1ull))] = bt[p];
+    if (keep) vt[off + __popcll(mask & ((1ull << lane) - 1ull))] = pid;
     kept += total;
     best1 = tile_max;
     __syncthreads();   // s_max and s_cnt are rewritten by the next tile
