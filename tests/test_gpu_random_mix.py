@@ -8,7 +8,9 @@ rows. Every output row is compared against the oracle (the page "[Kernel]
 and gates: randomized pages, ragged and boundary lengths). The same kind of
 mixtures also go through the paths that must agree bit for bit: the fused
 append + decode against append then decode, the no-alloc entry point against
-a handle, and graph replays against eager calls."""
+a handle, and graph replays against eager calls. A third test takes page
+subsets with selection rows longer than the selection kernel's 1,024-entry
+tile."""
 
 import numpy as np
 import pytest
@@ -188,3 +190,66 @@ def test_random_mixtures_bitwise_paths():
             assert torch.equal(out_g.view(torch.int16), out_sep.view(torch.int16)), f"{tag} replay {r}"
         del graph
         xqa.close()
+
+
+def test_random_page_subsets_over_several_tiles():
+    # Page-subset decode with selection rows longer than the selection
+    # kernel's 1,024-entry tile (up to 3,000 pages per sequence), selection
+    # strides below the handle's capacity, planted out-of-range, repeated and
+    # descending entries, and random counts; every row against the oracle,
+    # and selecting every page in order bitwise equal to plain decode.
+    ensure_library()
+    from decode_attention_paged_e5m2_amd import Xqa
+    rng = np.random.default_rng(4243)
+    for case in range(16):
+        hkv, g = SHAPES[case % len(SHAPES)]
+        batch = int(rng.choice([1, 2, 3]))
+        cap_pages = int(rng.choice([1100, 2100, 3000]))
+        cap = cap_pages * 16
+        ctx = rng.integers(1, cap + 1, batch)
+        ctx[rng.random(batch) < 0.2] = cap
+        w = make_custom(ctx.tolist(), hkv, hkv * g, [4243, case], max_pages_per_seq=cap_pages)
+        lens = ctx.copy()
+        lens[ctx == cap] += rng.integers(0, 3000, int((ctx == cap).sum()))   # clamped lengths
+        max_sel = cap_pages if case % 2 == 0 else int(rng.integers(1025, cap_pages + 1))
+        S = max_sel if case % 4 < 2 else int(rng.integers(1025, max_sel + 1))
+        sel = np.full((batch, S), -1, dtype=np.int32)
+        cnt = np.zeros(batch, dtype=np.int32)
+        for b in range(batch):
+            used = (min(int(lens[b]), cap) + 15) // 16
+            row = list(np.sort(rng.choice(used, size=min(int(rng.integers(0, S + 1)), used),
+                                          replace=False)))
+            for _ in range(3):
+                if len(row) < S:
+                    row.insert(int(rng.integers(0, len(row) + 1)), int(rng.integers(-3, used + 5)))
+            sel[b, :len(row)] = row
+            cnt[b] = len(row) if b != 1 else S + 7   # one count past the stride (clamped)
+        per_head = int(rng.choice([0, 2, 16]))
+        tag = f"case {case} B={batch} hkv={hkv} g={g} cap={cap_pages} S={S} max_sel={max_sel}"
+        print(tag, flush=True)
+        dev = to_device(w)
+        lt = torch.from_numpy(lens.astype(np.int32)).cuda()
+        xqa = Xqa(max_batch=batch, num_q_heads=hkv * g, num_kv_heads=hkv,
+                  max_pages_per_seq=cap_pages, max_work_items=hkv * per_head,
+                  max_selected_pages=max_sel)
+        out = xqa.decode_pages(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages,
+                               block_table=dev.block_table, context_lens=lt,
+                               page_select=torch.from_numpy(sel).cuda(),
+                               select_counts=torch.from_numpy(cnt).cuda(), scale=w.scale)
+        torch.cuda.synchronize()
+        kp, vp = w.pools()
+        ref = oracle.decode_attention_pages(w.q, kp, vp, w.block_table, lens, sel, cnt, w.scale)
+        assert_parity(out.float().cpu().numpy(), ref, tag)
+        if max_sel == cap_pages:
+            allp = torch.arange(cap_pages, dtype=torch.int32).repeat(batch, 1).cuda()
+            outa = xqa.decode_pages(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages,
+                                    block_table=dev.block_table, context_lens=lt, page_select=allp,
+                                    select_counts=torch.full((batch,), cap_pages,
+                                                             dtype=torch.int32).cuda(),
+                                    scale=w.scale)
+            outd = xqa.decode(q=dev.q, k_pages=dev.k_pages, v_pages=dev.v_pages,
+                              block_table=dev.block_table, context_lens=lt, scale=w.scale)
+            torch.cuda.synchronize()
+            assert torch.equal(outa.view(torch.int16), outd.view(torch.int16)), tag + " every page"
+        xqa.close()
+        del dev
