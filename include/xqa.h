@@ -256,7 +256,10 @@ xqa_status_t xqa_decode_append(xqa_handle_t handle, const void* q, const void* k
  * pages each query attends over. The page does not publish the selection
  * rule, so the selection is an input:
  *     page_select   int32 [batch][select_stride] logical page indices of sequence b
- *                   (index p covers tokens 16p .. 16p + 15), device memory
+ *                   (index p covers tokens 16p .. 16p + 15), device memory; every
+ *                   one of the batch x select_stride entries must be readable,
+ *                   whatever the counts (entries past a row's count are read and
+ *                   ignored)
  *     select_counts int32 [batch] entries of each row to use (clamped to [0, select_stride])
  * With n as for xqa_decode, an entry p is kept iff 0 <= p < ceil(n / 16) and
  * p is greater than every entry kept before it in its row (callers pass
