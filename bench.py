@@ -103,7 +103,7 @@ def log(msg):
 class ClockSampler:
     """Samples GPU clocks and power in a background thread while timed work runs.
 
-    Reads the driver's sysfs files (current shader / memory clock level and
+    Reads the amdgpu kernel driver's sysfs files (current shader / memory clock level and
     average power) every 20 ms; where they are not readable, rocm-smi (a
     child process) every 0.5 s. start()/stop() bracket the timed phases.
     """
