@@ -15,7 +15,7 @@ Recipe (fixed here because the pages give none; the design notes list it):
   (independent Bernoulli per element, multiplied by 1000), then rounded to
   E5M2 from float32, saturating at 57344;
 * pages: a seeded permutation of the pool; sequence b takes the next
-  ceil(n_b / P) entries in batch order (config 1: identity pages);
+  ceil(n_b / P) entries in batch order (the tiny B1 workload: identity pages);
 * pool = the stated number of data pages plus one poison page (the last);
   every byte not holding a real token (tail slots, unreferenced pages, the
   poison page) is the NaN code 0x7F, and unused block-table entries point at
@@ -168,7 +168,8 @@ def make_custom(context_lens: Sequence[int], num_kv_heads: int, num_q_heads: int
 
 def make_config(index: int, variant: int = 0, with_tokens: bool = True,
                 kv_format: str = "e5m2") -> Workload:
-    """Config 1..5 (see module docstring), deterministic in (index, variant).
+    """Workload 1..5 of CONFIG_NAMES (recipe in the module docstring),
+    deterministic in (index, variant).
 
     ``with_tokens=False`` stops after the block table and q (same draws), for
     callers that only need the shapes, lengths and page assignment.
