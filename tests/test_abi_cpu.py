@@ -104,3 +104,14 @@ def test_product_package_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(root, f)).read()
                 assert "oracle" not in re.sub(r"#.*|//.*", "", text).replace("oracle is", ""), f
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # Without the built library the product raises; there is no CPU path.
+    from decode_attention_paged_e5m2_amd import _lib, Xqa
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libxqa.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="is missing"):
+        _lib.load()
+    with pytest.raises(RuntimeError, match="is missing"):
+        Xqa(max_batch=1, num_q_heads=8, num_kv_heads=1, max_pages_per_seq=16)
